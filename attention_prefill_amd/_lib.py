@@ -1,0 +1,165 @@
+"""ctypes binding of libattn_mi355x.so (include/attn.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  Tensors are torch CUDA (HIP) tensors; torch supplies device memory
+and the current stream.  There is no fallback: if the library is not built,
+or a call fails, an exception says so.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn_mi355x.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+                4: "ATTN_ERR_ARG", 5: "ATTN_ERR_HIP"}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, str(status)), message))
+        self.status = status
+
+
+def load():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libattn_mi355x.so is not built (run __graft_entry__.build() or "
+                               "python attention_prefill_amd/build.py)")
+        lib = ctypes.CDLL(LIB_PATH)
+        fwd_args = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I]
+        lib.attn_fwd.argtypes = fwd_args
+        lib.attn_fwd.restype = _I
+        lib.attn_fwd_stream.argtypes = fwd_args + [_P]
+        lib.attn_fwd_stream.restype = _I
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_abi_version.argtypes = []
+        lib.attn_abi_version.restype = _I
+        lib.attn_debug_quantize_rows.argtypes = [_P, _I, _I, _P, _P, _I, _P]
+        lib.attn_debug_quantize_rows.restype = _I
+        lib.attn_debug_route_dump.argtypes = [_P, _I, _I, _I, _I, _P, _P]
+        lib.attn_debug_route_dump.restype = _I
+        _lib = lib
+    return _lib
+
+
+def attn_last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def attn_abi_version() -> int:
+    return load().attn_abi_version()
+
+
+def _check(status):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def attn_fwd_stream(q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal,
+                    cu_seqlens=None, route_bitmask=None, tiles_per_bit=4, stream=None):
+    """Direct mirror of the C entry point (sizes passed explicitly)."""
+    _check(load().attn_fwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, qsl, ksl, hdim, n_qh,
+                                  n_kvh, float(scale), int(bool(causal)), _ptr(cu_seqlens),
+                                  _ptr(route_bitmask), int(tiles_per_bit), _stream(stream)))
+
+
+def attn_fwd(q, k, v, out=None, *, scale=None, causal=False, cu_seqlens=None,
+             route_bitmask=None, tiles_per_bit=4, stream=None):
+    """Fused attention forward; sizes are read from the tensor shapes.
+
+    dense:  q [B, n_qh, qsl, d], k/v [B, n_kvh, ksl, d]
+    packed: q [n_qh, T, d], k/v [n_kvh, T, d], cu_seqlens int32 [B + 1]
+    route_bitmask: int32 / uint32-valued tensor of packed routing words.
+    Returns out (allocated when None).  Enqueued on torch's current stream.
+    """
+    import torch
+    _need(q, "q", torch.float16)
+    _need(k, "k", torch.float16)
+    _need(v, "v", torch.float16)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    if cu_seqlens is None:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("dense q/k/v must be 4-D [B, H, S, d]")
+        B, n_qh, qsl, d = q.shape
+        Bk, n_kvh, ksl, dk = k.shape
+        if Bk != B:
+            raise ValueError("q and k batch sizes differ")
+    else:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        if q.dim() != 3 or k.dim() != 3:
+            raise ValueError("packed q/k/v must be 3-D [H, T, d]")
+        n_qh, qsl, d = q.shape
+        n_kvh, ksl, dk = k.shape
+        B = cu_seqlens.numel() - 1
+    if dk != d:
+        raise ValueError("q and k head dims differ")
+    if route_bitmask is not None:
+        if route_bitmask.dtype not in (torch.int32, torch.uint32):
+            raise TypeError("route_bitmask must hold 32-bit words")
+        _need(route_bitmask, "route_bitmask", route_bitmask.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.float16)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    attn_fwd_stream(q, k, v, out, B, qsl, ksl, d, n_qh, n_kvh, scale, causal, cu_seqlens,
+                    route_bitmask, tiles_per_bit, stream)
+    return out
+
+
+def attn_debug_quantize_rows(x, path=0, stream=None):
+    """(q8 int8 [rows, d], s float32 [rows]) from the device quantiser."""
+    import torch
+    _need(x, "x", torch.float16)
+    rows, d = x.shape
+    q8 = torch.empty((rows, d), dtype=torch.int8, device=x.device)
+    s = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _check(load().attn_debug_quantize_rows(_ptr(x), rows, d, _ptr(q8), _ptr(s), int(path), _stream(stream)))
+    return q8, s
+
+
+def attn_debug_route_dump(route_bitmask, qsl, ksl, causal, tiles_per_bit, device="cuda", stream=None):
+    """uint8 [ceil(qsl/64), ceil(ksl/64)]: 0 FP16, 1 INT8, 2 not visited."""
+    import torch
+    n_qt, n_kt = -(-qsl // 64), -(-ksl // 64)
+    out = torch.empty((n_qt, n_kt), dtype=torch.uint8, device=device)
+    _check(load().attn_debug_route_dump(_ptr(route_bitmask), qsl, ksl, int(bool(causal)),
+                                        int(tiles_per_bit), _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,50 @@
+"""Builds the HIP library libattn_mi355x.so in-tree for gfx950 with hipcc."""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libattn_mi355x.so")
+SOURCES = ["attn_api.cpp", "attn_kernels.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # no packed-fp32 VALU instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
+def build(verbose: bool = False) -> str:
+    objs, procs = [], []
+    bdir = os.path.join(PKG, "_build")
+    os.makedirs(bdir, exist_ok=True)
+    for src in SOURCES:
+        obj = os.path.join(bdir, src + ".o")
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True))
+        objs.append(obj)
+    failed = False
+    for p in procs:
+        _, err = p.communicate()
+        err = "\n".join(ln for ln in err.splitlines()
+                        if "packed-fp32-ops" not in ln and "is not a recognized feature" not in ln)
+        if err.strip():
+            sys.stderr.write(err + "\n")
+        failed |= p.returncode != 0
+    if failed:
+        raise RuntimeError("hipcc failed")
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,142 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h: argument validation
+// (on the host, before any device work), scratch for routed calls, dispatch
+// to the kernel launchers, and error reporting.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "attn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status fail(attn_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+attn_status hip_fail(hipError_t e, const char* what) {
+    return fail(ATTN_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Checks every argument rule of include/attn.h; touches no device memory.
+attn_status validate(const attn::Problem& p) {
+    if (!p.q || !p.k || !p.v || !p.out)
+        return fail(ATTN_ERR_NULL, "q, k, v and out must be non-null device pointers");
+    if (p.B <= 0 || p.qsl <= 0 || p.ksl <= 0 || p.n_qh <= 0 || p.n_kvh <= 0)
+        return fail(ATTN_ERR_SHAPE, "B, qsl, ksl, n_qh, n_kvh must be positive (got %d, %d, %d, %d, %d)",
+                    p.B, p.qsl, p.ksl, p.n_qh, p.n_kvh);
+    if (p.n_qh % p.n_kvh != 0)
+        return fail(ATTN_ERR_SHAPE, "n_qh (%d) must be a multiple of n_kvh (%d)", p.n_qh, p.n_kvh);
+    if (p.causal && p.qsl > p.ksl)
+        return fail(ATTN_ERR_SHAPE, "causal attention needs qsl <= ksl (got %d > %d): rows would see no key",
+                    p.qsl, p.ksl);
+    if (p.cu_seqlens && p.qsl != p.ksl)
+        return fail(ATTN_ERR_SHAPE, "packed input needs qsl == ksl == total tokens (got %d, %d)", p.qsl, p.ksl);
+    if (p.hdim != 64 && p.hdim != 128)
+        return fail(ATTN_ERR_UNSUPPORTED, "hdim must be 64 or 128 (got %d)", p.hdim);
+    if (p.route && p.cu_seqlens)
+        return fail(ATTN_ERR_UNSUPPORTED, "a routing bitmask with packed (cu_seqlens) input is not supported");
+    if (!std::isfinite(p.scale) || p.scale == 0.0f)
+        return fail(ATTN_ERR_ARG, "scale must be finite and non-zero");
+    if (p.route && p.tiles_per_bit < 1)
+        return fail(ATTN_ERR_ARG, "tiles_per_bit must be >= 1 with a bitmask (got %d)", p.tiles_per_bit);
+    if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.out))
+        return fail(ATTN_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+    if ((p.cu_seqlens && !aligned4(p.cu_seqlens)) || (p.route && !aligned4(p.route)))
+        return fail(ATTN_ERR_ARG, "cu_seqlens and route_bitmask must be 4-byte aligned");
+    const double elems_q = (double)p.B * p.n_qh * p.qsl * p.hdim;
+    const double elems_k = (double)p.B * p.n_kvh * p.ksl * p.hdim;
+    if (elems_q > 9.0e15 || elems_k > 9.0e15 || (double)p.B * p.n_kvh * p.ksl > 2.0e9)
+        return fail(ATTN_ERR_SHAPE, "problem too large");
+    return ATTN_OK;
+}
+
+attn_status run_forward(const attn::Problem& p, hipStream_t st) {
+    attn_status vs = validate(p);
+    if (vs != ATTN_OK) return vs;
+    void* scratch = nullptr;
+    const size_t sbytes = attn::routed_scratch_bytes(p);
+    if (sbytes) {
+        hipError_t e = hipMallocAsync(&scratch, sbytes, st);
+        if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of routed scratch");
+    }
+    hipError_t e = attn::launch_forward(p, scratch, st);
+    if (scratch) {
+        hipError_t e2 = hipFreeAsync(scratch, st);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(e, "attention forward launch");
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_fwd_stream(const void* q, const void* k, const void* v, void* out, int32_t B,
+                            int32_t qsl, int32_t ksl, int32_t hdim, int32_t n_qh, int32_t n_kvh,
+                            float scale, int32_t causal, const int32_t* cu_seqlens,
+                            const uint32_t* route_bitmask, int32_t tiles_per_bit, void* hip_stream) {
+    attn::Problem p{q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal != 0,
+                    cu_seqlens, route_bitmask, tiles_per_bit};
+    return run_forward(p, (hipStream_t)hip_stream);
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* out, int32_t B,
+                     int32_t qsl, int32_t ksl, int32_t hdim, int32_t n_qh, int32_t n_kvh,
+                     float scale, int32_t causal, const int32_t* cu_seqlens,
+                     const uint32_t* route_bitmask, int32_t tiles_per_bit) {
+    return attn_fwd_stream(q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal, cu_seqlens,
+                           route_bitmask, tiles_per_bit, nullptr);
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+attn_status attn_debug_quantize_rows(const void* x_f16, int32_t rows, int32_t hdim, int8_t* q8,
+                                     float* scale_out, int32_t path, void* hip_stream) {
+    if (!x_f16 || !q8 || !scale_out) return fail(ATTN_ERR_NULL, "null pointer");
+    if (rows < 0) return fail(ATTN_ERR_SHAPE, "rows must be >= 0");
+    if (hdim != 64 && hdim != 128) return fail(ATTN_ERR_UNSUPPORTED, "hdim must be 64 or 128");
+    if (path != 0 && path != 1) return fail(ATTN_ERR_ARG, "path must be 0 or 1");
+    if (!aligned16(x_f16) || !aligned16(q8) || !aligned4(scale_out))
+        return fail(ATTN_ERR_ARG, "x and q8 must be 16-byte aligned, scale_out 4-byte aligned");
+    hipError_t e = attn::launch_quantize_rows(x_f16, rows, hdim, q8, scale_out, path, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
+attn_status attn_debug_route_dump(const uint32_t* route_bitmask, int32_t qsl, int32_t ksl,
+                                  int32_t causal, int32_t tiles_per_bit, uint8_t* route_out,
+                                  void* hip_stream) {
+    if (!route_out) return fail(ATTN_ERR_NULL, "route_out is null");
+    if (qsl <= 0 || ksl <= 0) return fail(ATTN_ERR_SHAPE, "qsl and ksl must be positive");
+    if (causal && qsl > ksl) return fail(ATTN_ERR_SHAPE, "causal needs qsl <= ksl");
+    if (tiles_per_bit < 1) return fail(ATTN_ERR_ARG, "tiles_per_bit must be >= 1");
+    if (route_bitmask && !aligned4(route_bitmask)) return fail(ATTN_ERR_ARG, "route_bitmask must be 4-byte aligned");
+    hipError_t e = attn::launch_route_dump(route_bitmask, qsl, ksl, causal != 0, tiles_per_bit, route_out,
+                                           (hipStream_t)hip_stream);
+    if (e != hipSuccess) return hip_fail(e, "route dump launch");
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
+}  // extern "C"

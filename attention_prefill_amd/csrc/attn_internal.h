@@ -1,0 +1,37 @@
+// attn_internal.h -- host-side interface between the C ABI (attn_api.cpp)
+// and the kernel launchers (attn_kernels.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// A validated forward problem (see include/attn.h for the meaning of each field).
+struct Problem {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    int B, qsl, ksl, hdim, n_qh, n_kvh;
+    float scale;
+    bool causal;
+    const int32_t* cu_seqlens;      // device, or nullptr
+    const uint32_t* route;          // device, or nullptr
+    int tiles_per_bit;
+};
+
+// Device scratch the routed path needs for quantised K rows (bytes).
+size_t routed_scratch_bytes(const Problem& p);
+
+// Enqueue the whole forward pass on stream.  scratch must hold
+// routed_scratch_bytes(p) bytes when p.route != nullptr (else may be null).
+hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t stream);
+
+// Test hooks (include/attn.h).
+hipError_t launch_quantize_rows(const void* x, int rows, int hdim, int8_t* q8, float* s,
+                                int path, hipStream_t stream);
+hipError_t launch_route_dump(const uint32_t* route, int qsl, int ksl, bool causal,
+                             int tiles_per_bit, uint8_t* out, hipStream_t stream);
+
+}  // namespace attn

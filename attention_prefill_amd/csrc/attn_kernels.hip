@@ -1,0 +1,719 @@
+// attn_kernels.hip -- fused attention forward (prefill) for gfx950 (MI355X).
+//
+// The operation is the fused scaled-dot-product attention timed in the
+// "Nax Refactor" page (ml-explore/mlx pull request 3271, fused vs unfused
+// timing tables), with the TileMix option (TileMix abstract): a bitmask
+// routes each (64-row query tile, group of 64-key tiles) through an FP16 or
+// an INT8 QK^T score computation, and both routes update one online-softmax
+// state (running max m, running sum l, fp32 output accumulator).
+//
+// Kernel structure (one workgroup = NW wavefronts of 64 lanes):
+//   * work decomposition: a workgroup owns HPW query heads of one kv head
+//     and BM = 32*NW/HPW query rows; every wavefront owns 32 rows of one
+//     head.  Grid order is heavy-first for causal masks and keeps the
+//     workgroups of one kv head on one XCD (index mod 8) when the number of
+//     head groups is a multiple of 8.
+//   * tile loader: 64-key K and V tiles go global -> registers -> LDS with
+//     two LDS stages, so the loads of tile t+1 are in flight while tile t is
+//     computed; one barrier per tile.
+//   * score MFMA: the transposed score tile S^T = K Q^T is computed with
+//     v_mfma_f32_32x32x16_f16 (FP16 route) or v_mfma_i32_32x32x32_i8 (INT8
+//     route).  In the 32x32 accumulator layout a lane then owns one query
+//     (column) and 16 keys, so row max / row sum are in-register plus one
+//     v_permlane32_swap between the two half-waves.  K rows are read with
+//     bits 2 and 3 of the row index swapped; this makes the score layout
+//     coincide with the B-operand layout of the P.V MFMA, so P never leaves
+//     registers.
+//   * P.V MFMA: O^T += V^T P^T with v_mfma_f32_32x32x16_f16, V^T fragments
+//     read from the natural [key][d] LDS layout by ds_read_b64_tr_b16.
+//   * online softmax in base 2 with the scale folded into one FMA per
+//     score; O is rescaled only when some row max of the wavefront moved.
+//   * INT8 route: K rows are quantised once per call by a separate pass
+//     (quantize_rows_kernel); the query rows of a wavefront are quantised in
+//     its prologue.  Per-token symmetric codes: s = fl32(amax/127),
+//     q = RNE(x * fl32(127/amax)) with the product exact (one FMA against
+//     1.5*2^23), int32 dot products, dequantised as dot * (s_k*c) * s_q.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BN = 64;          // keys per tile
+constexpr int TQ = 64;          // query rows per routing tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23
+
+// ---------------------------------------------------------------------------
+// INT8 quantisation rule shared by the K pass, the query prologue and the
+// test hook.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void quant_scale(float amax, float& s, float& inv) {
+    if (amax == 0.0f) {
+        s = 0.0f;
+        inv = 0.0f;
+    } else {
+        s = amax / 127.0f;       // IEEE division (no fast-math in this build)
+        inv = 127.0f / amax;
+    }
+}
+
+// round-half-even(x * inv) with the product exact: |x * inv| <= 127 + eps, so
+// x*inv + 1.5*2^23 lies in [2^23, 2^24) where the fp32 spacing is 1 and the
+// single rounding of the fused multiply-add is the integer rounding; the
+// even offset keeps ties at even.
+__device__ __forceinline__ int quant_code(float x, float inv) {
+    float r = __builtin_fmaf(x, inv, RNE_MAGIC) - RNE_MAGIC;
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+__device__ __forceinline__ float f_from_u(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned u_from_f(float f) { return __builtin_bit_cast(unsigned, f); }
+
+// max of a value over lanes l and l^32
+__device__ __forceinline__ float halfwave_max(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(u_from_f(v), u_from_f(v), false, false);
+    return fmaxf(f_from_u(r[0]), f_from_u(r[1]));
+}
+
+__device__ __forceinline__ float halfwave_sum(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(u_from_f(v), u_from_f(v), false, false);
+    return f_from_u(r[0]) + f_from_u(r[1]);
+}
+
+// Query rows held in the score B-operand layout: lane l (g = l/32) holds
+// Q[row l%32][32*kb + 16*g + 8*e + j] in qf[2*kb + e][j].  The INT8 operand
+// for k-step ks holds the 16 codes of d = 32*ks + 16*g + j, j = 0..15.
+template <int HD>
+__device__ __forceinline__ void quantize_q_regs(const f16x8 (&qf)[HD / 16], i32x4 (&q8)[HD / 32],
+                                                float& s_out) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int t = 0; t < HD / 16; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)qf[t][j]));
+    amax = halfwave_max(amax);
+    float s, inv;
+    quant_scale(amax, s, inv);
+#pragma unroll
+    for (int ks = 0; ks < HD / 32; ++ks) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            unsigned word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                int j = 4 * w + b;
+                int c = quant_code((float)qf[2 * ks + j / 8][j % 8], inv);
+                word |= ((unsigned)c & 0xffu) << (8 * b);
+            }
+            q8[ks][w] = (int)word;
+        }
+    }
+    s_out = s;
+}
+
+// ---------------------------------------------------------------------------
+// Routing decode: bit of group kt / tiles_per_bit in the row of query tile qt.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool route_bit(const uint32_t* row, int kt, int tiles_per_bit) {
+    int gi = kt / tiles_per_bit;
+    return (row[gi >> 5] >> (gi & 31)) & 1u;
+}
+
+// ---------------------------------------------------------------------------
+// LDS layout of one stage: K tile (fp16, or INT8 codes + scaled s_k) then V.
+// Row pitches are padded so that the row-parallel reads of the MFMA operands
+// spread over the banks.
+// ---------------------------------------------------------------------------
+template <int HD>
+struct Lds {
+    static constexpr int KP = HD + 8;            // fp16 elements per K row
+    static constexpr int VP = HD + 16;           // fp16 elements per V row
+    static constexpr int K8P = HD + 16;          // bytes per INT8 K row
+    static constexpr int KBYTES = BN * KP * 2;
+    static constexpr int K8BYTES = BN * K8P + BN * 4;
+    static constexpr int KREG = KBYTES > K8BYTES ? KBYTES : K8BYTES;
+    static constexpr int VBYTES = BN * VP * 2;
+    static constexpr int STAGE = KREG + VBYTES;
+    static constexpr int TOTAL = 2 * STAGE;
+};
+
+struct FwdArgs {
+    const _Float16* q;
+    const _Float16* k;
+    const _Float16* v;
+    _Float16* out;
+    const int8_t* k8;       // quantised K rows (routed), same row order as k
+    const float* sk;        // their scales
+    const int32_t* cu;      // packed sequence offsets, or null
+    const uint32_t* route;  // routing bitmask, or null
+    int B, qsl, ksl, n_qh, n_kvh, G, HPW;
+    int combos;             // workgroup columns: (batch x) kv heads x head groups
+    int n_mblk;             // query blocks per column (packed: upper bound)
+    int tiles_per_bit, wpr;
+    float c;                // |scale| * log2(e)
+    int neg;                // scale < 0: queries are negated
+};
+
+// ---------------------------------------------------------------------------
+// Fused forward kernel.
+// ---------------------------------------------------------------------------
+template <int HD, int NW, bool CAUSAL, bool VARLEN, bool ROUTED>
+__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
+    using L = Lds<HD>;
+    constexpr int NT = NW * 64;
+    constexpr int KCH = BN * HD / 8 / NT;      // 16-byte fp16 chunks per thread (K or V)
+    constexpr int K8CH = BN * HD / 16 / NT;    // 16-byte INT8 chunks per thread
+    constexpr int NDB = HD / 32;               // 32-row blocks of d in O^T
+    static_assert(KCH >= 1 && K8CH >= 1, "tile too small for the workgroup");
+
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int l = tid & 63;
+    const int g = l >> 5;
+    const int lq = l & 31;
+    const int HPW = a.HPW;
+    const int BM = (NW / HPW) * 32;
+
+    // ---- work decomposition -------------------------------------------------
+    const int combo = blockIdx.x % a.combos;
+    const int rank = blockIdx.x / a.combos;
+    const int hpc = a.G / HPW;
+    const int hsub = combo % hpc;
+    const int hk = (combo / hpc) % a.n_kvh;
+    const int h = hk * a.G + hsub * HPW + (w % HPW);
+
+    int mb, Lq, Lk;
+    size_t qrow0, krow0;            // row index of row 0 of (sequence, head) in q / k
+    if constexpr (VARLEN) {
+        int t = rank, s = -1;
+        mb = 0;
+        for (int ss = a.B - 1; ss >= 0; --ss) {
+            int Ls = a.cu[ss + 1] - a.cu[ss];
+            int nb = (Ls + BM - 1) / BM;
+            if (t < nb) { s = ss; mb = nb - 1 - t; break; }
+            t -= nb;
+        }
+        if (s < 0) return;          // uniform for the workgroup, before any barrier
+        const int start = a.cu[s];
+        const int T = a.cu[a.B];
+        Lq = Lk = a.cu[s + 1] - start;
+        qrow0 = (size_t)h * T + start;
+        krow0 = (size_t)hk * T + start;
+    } else {
+        const int b = combo / (hpc * a.n_kvh);
+        mb = CAUSAL ? (a.n_mblk - 1 - rank) : rank;
+        Lq = a.qsl;
+        Lk = a.ksl;
+        qrow0 = ((size_t)b * a.n_qh + h) * Lq;
+        krow0 = ((size_t)b * a.n_kvh + hk) * Lk;
+    }
+    const _Float16* qb = a.q + qrow0 * HD;
+    _Float16* ob = a.out + qrow0 * HD;
+    const _Float16* kb = a.k + krow0 * HD;
+    const _Float16* vb = a.v + krow0 * HD;
+    const int8_t* k8b = ROUTED ? a.k8 + krow0 * HD : nullptr;
+    const float* skb = ROUTED ? a.sk + krow0 : nullptr;
+
+    const int off = CAUSAL ? (Lk - Lq) : 0;     // bottom-right alignment
+    const int m0 = mb * BM;
+    const int r0 = m0 + (w / HPW) * 32;          // first row of this wavefront
+    const int n_kt = (Lk + BN - 1) / BN;
+    const int wg_last = min(m0 + BM, Lq) - 1;
+    const int nkt = CAUSAL ? min(n_kt, (wg_last + off) / BN + 1) : n_kt;
+    const bool wave_active = r0 < Lq;
+    const int w_nkt = !wave_active ? 0
+                    : CAUSAL ? min(n_kt, (min(r0 + 31, Lq - 1) + off) / BN + 1) : n_kt;
+
+    const uint32_t* rrow = ROUTED ? a.route + (size_t)(m0 / TQ) * a.wpr : nullptr;
+
+    // ---- query rows into the score B-operand layout ---------------------------
+    f16x8 qf[HD / 16];
+    {
+        const int qi = r0 + lq;
+        const _Float16* qp = qb + (size_t)qi * HD + 16 * g;
+#pragma unroll
+        for (int kb2 = 0; kb2 < HD / 32; ++kb2) {
+            if (qi < Lq) {
+                qf[2 * kb2] = *(const f16x8*)(qp + 32 * kb2);
+                qf[2 * kb2 + 1] = *(const f16x8*)(qp + 32 * kb2 + 8);
+            } else {
+                qf[2 * kb2] = f16x8{};
+                qf[2 * kb2 + 1] = f16x8{};
+            }
+        }
+        if (a.neg) {
+#pragma unroll
+            for (int t = 0; t < HD / 16; ++t) qf[t] = -qf[t];
+        }
+    }
+    i32x4 q8[ROUTED ? HD / 32 : 1];
+    float sq_mul = 1.0f;
+    if constexpr (ROUTED) {
+        float sq;
+        quantize_q_regs<HD>(qf, q8, sq);
+        sq_mul = sq > 0.0f ? sq : 1.0f;   // a zero row has all-zero INT8 scores
+    }
+
+    // ---- tile loader ------------------------------------------------------------
+    uint4 kreg[KCH], vreg[KCH];
+    float skreg[4];
+
+    auto gload = [&](int kt, bool i8) {
+        const int key0 = kt * BN;
+        if (ROUTED && i8) {
+#pragma unroll
+            for (int n = 0; n < K8CH; ++n) {
+                const int c = tid + n * NT;
+                const int row = c / (HD / 16);
+                const int col = (c % (HD / 16)) * 16;
+                const int key = key0 + row;
+                kreg[n] = key < Lk ? *(const uint4*)(k8b + (size_t)key * HD + col) : uint4{0, 0, 0, 0};
+            }
+            if (tid < BN / 4) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = key0 + 4 * tid + e;
+                    skreg[e] = key < Lk ? skb[key] : 0.0f;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < KCH; ++n) {
+                const int c = tid + n * NT;
+                const int row = c / (HD / 8);
+                const int col = (c % (HD / 8)) * 8;
+                const int key = key0 + row;
+                kreg[n] = key < Lk ? *(const uint4*)(kb + (size_t)key * HD + col) : uint4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < KCH; ++n) {
+            const int c = tid + n * NT;
+            const int row = c / (HD / 8);
+            const int col = (c % (HD / 8)) * 8;
+            const int key = key0 + row;
+            vreg[n] = key < Lk ? *(const uint4*)(vb + (size_t)key * HD + col) : uint4{0, 0, 0, 0};
+        }
+    };
+
+    auto lstore = [&](int stage, bool i8) {
+        char* kbuf = smem + stage * L::STAGE;
+        _Float16* vbuf = (_Float16*)(kbuf + L::KREG);
+        if (ROUTED && i8) {
+#pragma unroll
+            for (int n = 0; n < K8CH; ++n) {
+                const int c = tid + n * NT;
+                const int row = c / (HD / 16);
+                const int col = (c % (HD / 16)) * 16;
+                *(uint4*)(kbuf + row * L::K8P + col) = kreg[n];
+            }
+            if (tid < BN / 4) {
+                float* skc = (float*)(kbuf + BN * L::K8P);
+                *(f32x4*)(skc + 4 * tid) = f32x4{skreg[0] * a.c, skreg[1] * a.c, skreg[2] * a.c, skreg[3] * a.c};
+            }
+        } else {
+            _Float16* k16 = (_Float16*)kbuf;
+#pragma unroll
+            for (int n = 0; n < KCH; ++n) {
+                const int c = tid + n * NT;
+                const int row = c / (HD / 8);
+                const int col = (c % (HD / 8)) * 8;
+                *(uint4*)(k16 + row * L::KP + col) = kreg[n];
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < KCH; ++n) {
+            const int c = tid + n * NT;
+            const int row = c / (HD / 8);
+            const int col = (c % (HD / 8)) * 8;
+            *(uint4*)(vbuf + row * L::VP + col) = vreg[n];
+        }
+    };
+
+    // ---- state --------------------------------------------------------------------
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    float m_run = -INFINITY;
+    float l_run = 0.0f;
+
+    // K row read by this lane for the score A operand: bits 2 and 3 swapped
+    const int krow = (lq & ~12) | ((lq & 4) << 1) | ((lq & 8) >> 1);
+    const int qi = r0 + lq;
+
+    bool i8_next = ROUTED && nkt > 0 && route_bit(rrow, 0, a.tiles_per_bit);
+    if (nkt > 0) {
+        gload(0, i8_next);
+        lstore(0, i8_next);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nkt; ++kt) {
+        const bool i8_cur = i8_next;
+        const bool more = kt + 1 < nkt;
+        i8_next = ROUTED && more && route_bit(rrow, kt + 1, a.tiles_per_bit);
+        if (more) gload(kt + 1, i8_next);
+
+        if (kt < w_nkt) {
+            const char* kbuf = smem + (kt & 1) * L::STAGE;
+            const _Float16* vbuf = (const _Float16*)(kbuf + L::KREG);
+            float x[2][16];
+            float amul;
+            // -- scores S^T = K Q^T for the two 32-key blocks of the tile
+            if (ROUTED && i8_cur) {
+                const float* skc = (const float*)(kbuf + BN * L::K8P);
+#pragma unroll
+                for (int kb32 = 0; kb32 < 2; ++kb32) {
+                    i32x16 acc = i32x16{};
+                    const int8_t* kr = (const int8_t*)kbuf + (32 * kb32 + krow) * L::K8P + 16 * g;
+#pragma unroll
+                    for (int ks = 0; ks < HD / 32; ++ks) {
+                        i32x4 av = *(const i32x4*)(kr + 32 * ks);
+                        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, q8[ks], acc, 0, 0, 0);
+                    }
+                    // lane's keys: 32*kb32 + 8*g + (i%8) + 16*(i/8)
+                    const float* sp = skc + 32 * kb32 + 8 * g;
+                    f32x4 s0 = *(const f32x4*)(sp);
+                    f32x4 s1 = *(const f32x4*)(sp + 4);
+                    f32x4 s2 = *(const f32x4*)(sp + 16);
+                    f32x4 s3 = *(const f32x4*)(sp + 20);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        x[kb32][i] = (float)acc[i] * s0[i];
+                        x[kb32][4 + i] = (float)acc[4 + i] * s1[i];
+                        x[kb32][8 + i] = (float)acc[8 + i] * s2[i];
+                        x[kb32][12 + i] = (float)acc[12 + i] * s3[i];
+                    }
+                }
+                amul = sq_mul;
+            } else {
+                const _Float16* k16 = (const _Float16*)kbuf;
+#pragma unroll
+                for (int kb32 = 0; kb32 < 2; ++kb32) {
+                    f32x16 acc = f32x16{};
+                    const _Float16* kr = k16 + (32 * kb32 + krow) * L::KP + 16 * g;
+#pragma unroll
+                    for (int t = 0; t < HD / 16; ++t) {
+                        f16x8 av = *(const f16x8*)(kr + 32 * (t / 2) + 8 * (t % 2));
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[t], acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) x[kb32][i] = acc[i];
+                }
+                amul = a.c;
+            }
+
+            // -- mask: keys past the end, and the bottom-right causal boundary
+            const int key0 = kt * BN;
+            const bool need_mask = (key0 + BN > Lk) || (CAUSAL && key0 + BN - 1 > r0 + off);
+            if (need_mask) {
+                const int lim = CAUSAL ? min(Lk - 1, qi + off) : Lk - 1;
+#pragma unroll
+                for (int kb32 = 0; kb32 < 2; ++kb32)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = key0 + 32 * kb32 + 8 * g + (i % 8) + 16 * (i / 8);
+                        if (key > lim) x[kb32][i] = -INFINITY;
+                    }
+            }
+
+            // -- online softmax (base 2)
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb32 = 0; kb32 < 2; ++kb32)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mt = fmaxf(mt, x[kb32][i]);
+            mt = halfwave_max(mt);
+            const float m_new = fmaxf(m_run, mt * amul);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            m_run = m_new;
+
+            f16x8 pk[2][2];
+            float rs = 0.0f;
+#pragma unroll
+            for (int kb32 = 0; kb32 < 2; ++kb32)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb32][8 * t + j], amul, -m_use));
+                        rs += p;
+                        pk[kb32][t][j] = (_Float16)p;
+                    }
+            l_run = l_run * alpha + rs;
+            if (__any(alpha != 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+            }
+
+            // -- O^T += V^T P^T
+            const int vr = 8 * g + ((l & 15) >> 2);
+            const int vc = 16 * ((l >> 4) & 1) + 4 * (l & 3);
+#pragma unroll
+            for (int kb32 = 0; kb32 < 2; ++kb32)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const _Float16* vp = vbuf + (32 * kb32 + 16 * t + vr) * L::VP + vc;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * db));
+                        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * db + 4 * L::VP));
+                        f16x4 flo = __builtin_bit_cast(f16x4, lo);
+                        f16x4 fhi = __builtin_bit_cast(f16x4, hi);
+                        f16x8 av = __builtin_shufflevector(flo, fhi, 0, 1, 2, 3, 4, 5, 6, 7);
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[kb32][t], o[db], 0, 0, 0);
+                    }
+                }
+        }
+
+        if (more) lstore((kt + 1) & 1, i8_next);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O / l -> fp16 ---------------------------------------------------
+    const float l_tot = halfwave_sum(l_run);
+    if (wave_active && qi < Lq) {
+        const float inv_l = 1.0f / l_tot;
+        _Float16* op = ob + (size_t)qi * HD + 4 * g;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                f16x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(o[db][4 * r + e] * inv_l);
+                *(f16x4*)(op + 32 * db + 8 * r) = hv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K-row quantisation pass (and test hook path 0): rows of HD fp16 values,
+// HD/8 lanes per row, 8 values per lane.
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const _Float16* __restrict__ x,
+                                                            int8_t* __restrict__ q8,
+                                                            float* __restrict__ s, long long rows) {
+    constexpr int LPR = HD / 8;
+    const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long row = gt / LPR;
+    const int part = (int)(gt % LPR);
+    const bool ok = row < rows;
+    f16x8 v = ok ? *(const f16x8*)(x + row * HD + part * 8) : f16x8{};
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)v[j]));
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    float sc, inv;
+    quant_scale(amax, sc, inv);
+    unsigned w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        w0 |= ((unsigned)quant_code((float)v[j], inv) & 0xffu) << (8 * j);
+        w1 |= ((unsigned)quant_code((float)v[4 + j], inv) & 0xffu) << (8 * j);
+    }
+    if (ok) {
+        *(uint2*)(q8 + row * HD + part * 8) = uint2{w0, w1};
+        if (part == 0) s[row] = sc;
+    }
+}
+
+// Test hook path 1: the query prologue quantiser on 32-row blocks.
+template <int HD>
+__global__ __launch_bounds__(64) void quantize_qrows_kernel(const _Float16* __restrict__ x,
+                                                            int8_t* __restrict__ q8,
+                                                            float* __restrict__ s, int rows) {
+    const int l = threadIdx.x, g = l >> 5, lq = l & 31;
+    const int row = blockIdx.x * 32 + lq;
+    f16x8 qf[HD / 16];
+    const _Float16* qp = x + (size_t)row * HD + 16 * g;
+#pragma unroll
+    for (int kb2 = 0; kb2 < HD / 32; ++kb2) {
+        qf[2 * kb2] = row < rows ? *(const f16x8*)(qp + 32 * kb2) : f16x8{};
+        qf[2 * kb2 + 1] = row < rows ? *(const f16x8*)(qp + 32 * kb2 + 8) : f16x8{};
+    }
+    i32x4 q8r[HD / 32];
+    float sc;
+    quantize_q_regs<HD>(qf, q8r, sc);
+    if (row < rows) {
+#pragma unroll
+        for (int ks = 0; ks < HD / 32; ++ks)
+            *(i32x4*)(q8 + (size_t)row * HD + 32 * ks + 16 * g) = q8r[ks];
+        if (g == 0) s[row] = sc;
+    }
+}
+
+// Test hook: the route each (query tile, key tile) takes in the forward kernel.
+__global__ void route_dump_kernel(const uint32_t* route, int qsl, int ksl, int causal,
+                                  int tiles_per_bit, int wpr, uint8_t* out) {
+    const int n_kt = (ksl + BN - 1) / BN;
+    const int n_qt = (qsl + TQ - 1) / TQ;
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long long)n_qt * n_kt) return;
+    const int qt = (int)(idx / n_kt), kt = (int)(idx % n_kt);
+    const int last_row = min(qt * TQ + TQ, qsl) - 1;
+    const bool visited = !causal || kt * BN <= last_row + (ksl - qsl);
+    uint8_t r = 2;
+    if (visited) r = (route != nullptr && route_bit(route + (size_t)qt * wpr, kt, tiles_per_bit)) ? 1 : 0;
+    out[idx] = r;
+}
+
+template <typename K>
+hipError_t set_lds(K kernel, int bytes) {
+    return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int HD, int NW, bool CAUSAL, bool VARLEN, bool ROUTED>
+hipError_t launch_fwd_t(const FwdArgs& a, int grid, hipStream_t st) {
+    auto kern = attn_fwd_kernel<HD, NW, CAUSAL, VARLEN, ROUTED>;
+    constexpr int lds = Lds<HD>::TOTAL;
+    hipError_t e = set_lds(kern, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int HD, int NW>
+hipError_t dispatch_flags(const FwdArgs& a, int grid, bool causal, bool varlen, bool routed,
+                          hipStream_t st) {
+    if (routed) {
+        // routed packed batches are rejected by the ABI
+        return causal ? launch_fwd_t<HD, NW, true, false, true>(a, grid, st)
+                      : launch_fwd_t<HD, NW, false, false, true>(a, grid, st);
+    }
+    if (varlen)
+        return causal ? launch_fwd_t<HD, NW, true, true, false>(a, grid, st)
+                      : launch_fwd_t<HD, NW, false, true, false>(a, grid, st);
+    return causal ? launch_fwd_t<HD, NW, true, false, false>(a, grid, st)
+                  : launch_fwd_t<HD, NW, false, false, false>(a, grid, st);
+}
+
+}  // namespace
+
+size_t routed_scratch_bytes(const Problem& p) {
+    if (!p.route) return 0;
+    const size_t rows = (size_t)p.B * p.n_kvh * p.ksl;
+    const size_t k8 = (rows * p.hdim + 255) / 256 * 256;
+    return k8 + rows * sizeof(float);
+}
+
+hipError_t launch_quantize_rows(const void* x, int rows, int hdim, int8_t* q8, float* s,
+                                int path, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    if (path == 0) {
+        const long long threads = (long long)rows * (hdim / 8);
+        const int grid = (int)((threads + 255) / 256);
+        if (hdim == 64)
+            hipLaunchKernelGGL(quantize_rows_kernel<64>, dim3(grid), dim3(256), 0, st,
+                               (const _Float16*)x, q8, s, (long long)rows);
+        else
+            hipLaunchKernelGGL(quantize_rows_kernel<128>, dim3(grid), dim3(256), 0, st,
+                               (const _Float16*)x, q8, s, (long long)rows);
+    } else {
+        const int grid = (rows + 31) / 32;
+        if (hdim == 64)
+            hipLaunchKernelGGL(quantize_qrows_kernel<64>, dim3(grid), dim3(64), 0, st,
+                               (const _Float16*)x, q8, s, rows);
+        else
+            hipLaunchKernelGGL(quantize_qrows_kernel<128>, dim3(grid), dim3(64), 0, st,
+                               (const _Float16*)x, q8, s, rows);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_route_dump(const uint32_t* route, int qsl, int ksl, bool causal,
+                             int tiles_per_bit, uint8_t* out, hipStream_t st) {
+    const int n_kt = (ksl + BN - 1) / BN;
+    const int n_qt = (qsl + TQ - 1) / TQ;
+    const int n_g = (n_kt + tiles_per_bit - 1) / tiles_per_bit;
+    const int wpr = (n_g + 31) / 32;
+    const long long n = (long long)n_qt * n_kt;
+    const int grid = (int)((n + 255) / 256);
+    hipLaunchKernelGGL(route_dump_kernel, dim3(grid), dim3(256), 0, st, route, qsl, ksl,
+                       causal ? 1 : 0, tiles_per_bit, wpr, out);
+    return hipGetLastError();
+}
+
+static int largest_div(int G, int cap) {
+    for (int d = cap; d > 1; d >>= 1)
+        if (G % d == 0) return d;
+    return 1;
+}
+
+hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
+    FwdArgs a;
+    a.q = (const _Float16*)p.q;
+    a.k = (const _Float16*)p.k;
+    a.v = (const _Float16*)p.v;
+    a.out = (_Float16*)p.out;
+    a.cu = p.cu_seqlens;
+    a.route = p.route;
+    a.B = p.B;
+    a.qsl = p.qsl;
+    a.ksl = p.ksl;
+    a.n_qh = p.n_qh;
+    a.n_kvh = p.n_kvh;
+    a.G = p.n_qh / p.n_kvh;
+    a.c = fabsf(p.scale) * LOG2E;
+    a.neg = p.scale < 0.0f ? 1 : 0;
+    a.tiles_per_bit = p.route ? p.tiles_per_bit : 1;
+    a.k8 = nullptr;
+    a.sk = nullptr;
+    const bool varlen = p.cu_seqlens != nullptr;
+    const bool routed = p.route != nullptr;
+
+    // workgroup shape: a routed workgroup stays inside one 64-row query tile
+    int NW = 4;
+    int HPW = largest_div(a.G, 4);
+    if (routed && HPW == 1) NW = 2;
+    a.HPW = HPW;
+    const int BM = (NW / HPW) * 32;
+    const int hpc = a.G / HPW;
+    a.combos = (varlen ? 1 : p.B) * p.n_kvh * hpc;
+    a.n_mblk = varlen ? (p.qsl + BM - 1) / BM + p.B : (p.qsl + BM - 1) / BM;
+
+    if (routed) {
+        const int n_kt = (p.ksl + BN - 1) / BN;
+        const int n_g = (n_kt + p.tiles_per_bit - 1) / p.tiles_per_bit;
+        a.wpr = (n_g + 31) / 32;
+        const size_t rows = (size_t)p.B * p.n_kvh * p.ksl;
+        const size_t k8bytes = (rows * p.hdim + 255) / 256 * 256;
+        a.k8 = (const int8_t*)scratch;
+        a.sk = (const float*)((char*)scratch + k8bytes);
+        hipError_t e = launch_quantize_rows(p.k, (int)rows, p.hdim, (int8_t*)a.k8, (float*)a.sk, 0, st);
+        if (e != hipSuccess) return e;
+    } else {
+        a.wpr = 0;
+    }
+
+    const long long grid_ll = (long long)a.combos * a.n_mblk;
+    if (grid_ll <= 0) return hipSuccess;
+    if (grid_ll > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int grid = (int)grid_ll;
+    if (p.hdim == 64)
+        return NW == 4 ? dispatch_flags<64, 4>(a, grid, p.causal, varlen, routed, st)
+                       : dispatch_flags<64, 2>(a, grid, p.causal, varlen, routed, st);
+    return NW == 4 ? dispatch_flags<128, 4>(a, grid, p.causal, varlen, routed, st)
+                   : dispatch_flags<128, 2>(a, grid, p.causal, varlen, routed, st);
+}
+
+}  // namespace attn

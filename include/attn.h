@@ -1,0 +1,110 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention-forward (prefill)
+ * library, libattn_mi355x.so.
+ *
+ * The operation (attn_fwd) is fused scaled-dot-product attention forward,
+ * as timed in the "Nax Refactor" page (ml-explore/mlx pull request 3271,
+ * fused-vs-unfused timing tables over B, qsl, ksl, hdim, n_qh, n_kvh, causal
+ * in float16), with the TileMix option (TileMix abstract, Lattice paper
+ * summary): a compact bitmask routes each (query tile, key-tile group)
+ * through an FP16 or an INT8 QK^T score computation, and both routes update
+ * one online-softmax state.
+ *
+ * For every batch element (or packed sequence) s, query head h, row i:
+ *   out[s,h,i,:] = sum_j softmax_j(S[i,j]) * v[s,hk,j,:],  hk = h / (n_qh/n_kvh)
+ *   S[i,j] = scale * <q[s,h,i,:], k[s,hk,j,:]>                 (FP16 route)
+ *   S[i,j] = scale * s_q[i] * s_k[j] * <q8[s,h,i,:], k8[s,hk,j,:]>  (INT8 route)
+ * over the visible keys j: all j < ksl, or, when causal, j <= i + (ksl - qsl)
+ * (bottom-right aligned).  INT8 codes are per token: amax = max_d |x_d|,
+ * s = fl32(amax / 127), q8_d = round-half-even(x_d * fl32(127 / amax)) with
+ * the product exact; a zero row has s = 0 and q8 = 0.  V stays fp16.
+ *
+ * Memory: every tensor pointer is DEVICE memory owned by the caller,
+ * contiguous, 16-byte aligned.  fp16 is IEEE binary16.
+ *   dense  (cu_seqlens == NULL): q, out [B, n_qh, qsl, hdim]; k, v [B, n_kvh, ksl, hdim]
+ *   packed (cu_seqlens != NULL): q, out [n_qh, T, hdim];    k, v [n_kvh, T, hdim]
+ *     with T = qsl = ksl and cu_seqlens int32 [B + 1] on the device,
+ *     cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = T.  Each sequence is
+ *     its own attention problem (causal per sequence when causal != 0).
+ * route_bitmask (device, uint32, may be NULL = every tile FP16): one bit per
+ *   (64-row query tile qt, group g of tiles_per_bit adjacent 64-key tiles),
+ *   shared by all heads and batch elements.  Rows of wpr = ceil(n_g / 32)
+ *   words, n_g = ceil(ceil(ksl / 64) / tiles_per_bit); bit g of row qt is
+ *   (route_bitmask[qt * wpr + g / 32] >> (g % 32)) & 1; 1 = INT8, 0 = FP16.
+ *   Tile indices count from row 0 of q and row 0 of k.  Bits of groups that
+ *   the causal mask leaves empty for a query tile are ignored.
+ * out is fully overwritten.  Nothing the caller passes is retained.
+ *
+ * Calls are asynchronous: they validate the arguments on the host, enqueue
+ * work on the given stream and return.  A routed call uses stream-ordered
+ * device scratch (hipMallocAsync / hipFreeAsync on the same stream) for the
+ * quantised K rows.  Errors are reported by the return code; a
+ * thread-local message is available from attn_last_error().  Argument
+ * errors are detected before any device work is enqueued.
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,         /* q, k, v or out is NULL */
+    ATTN_ERR_SHAPE = 2,        /* a size <= 0, n_qh % n_kvh != 0, causal with
+                                  qsl > ksl, or packed with qsl != ksl */
+    ATTN_ERR_UNSUPPORTED = 3,  /* hdim not 64 or 128; bitmask with cu_seqlens */
+    ATTN_ERR_ARG = 4,          /* scale not finite or zero; tiles_per_bit < 1
+                                  with a bitmask; pointer not 16-byte aligned */
+    ATTN_ERR_HIP = 5           /* the HIP runtime reported an error */
+} attn_status;
+
+#define ATTN_ABI_VERSION 1
+
+/* Fused attention forward on the null (default) stream.  scale may be
+ * negative; tiles_per_bit is read only when route_bitmask != NULL. */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* out,
+                     int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
+                     int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                     const int32_t* cu_seqlens, const uint32_t* route_bitmask,
+                     int32_t tiles_per_bit);
+
+/* Same, enqueued on hip_stream (a hipStream_t; NULL = null stream). */
+attn_status attn_fwd_stream(const void* q, const void* k, const void* v, void* out,
+                            int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
+                            int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                            const int32_t* cu_seqlens, const uint32_t* route_bitmask,
+                            int32_t tiles_per_bit, void* hip_stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The string is owned by the library and valid until the next call. */
+const char* attn_last_error(void);
+
+/* ATTN_ABI_VERSION of the loaded library. */
+int32_t attn_abi_version(void);
+
+/* Test hooks for bit-exact checks of the INT8 quantiser (same rule as above).
+ * x_f16: device [rows, hdim] fp16; q8: device int8 [rows, hdim]; scale_out:
+ * device fp32 [rows].  path 0 runs the K-row quantiser used before routed
+ * calls, path 1 the query-row quantiser of the attention prologue.
+ * Asynchronous on hip_stream. */
+attn_status attn_debug_quantize_rows(const void* x_f16, int32_t rows, int32_t hdim,
+                                     int8_t* q8, float* scale_out, int32_t path,
+                                     void* hip_stream);
+
+/* Test hook for the routing decode: writes, for every (query tile qt, key
+ * tile kt) of a qsl x ksl problem, the route the attention kernel takes:
+ * 0 = FP16, 1 = INT8, 2 = not visited (the causal mask leaves that tile
+ * empty for every row of qt).  route_out: device uint8 [ceil(qsl/64),
+ * ceil(ksl/64)].  Asynchronous on hip_stream. */
+attn_status attn_debug_route_dump(const uint32_t* route_bitmask, int32_t qsl, int32_t ksl,
+                                  int32_t causal, int32_t tiles_per_bit, uint8_t* route_out,
+                                  void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_MI355X_H */

@@ -1,0 +1,95 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/attn.h declares, and rejects bad arguments with the documented codes
+before touching the device (every pointer below is a fake, never read)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_prefill_amd as A
+from attention_prefill_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, UNSUP, ARG = 0, 1, 2, 3, 4
+FAKE = 0x10000          # 16-byte aligned, never dereferenced on error paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ["attn_fwd", "attn_fwd_stream", "attn_last_error", "attn_abi_version",
+              "attn_debug_quantize_rows", "attn_debug_route_dump"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_abi_version():
+    assert A.attn_abi_version() == 1
+
+
+def call(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, qsl=64, ksl=64, hdim=64, n_qh=4, n_kvh=2,
+         scale=0.125, causal=0, cu=None, route=None, tpb=4):
+    lib = A.load()
+    return lib.attn_fwd(q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal, cu, route, tpb)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(out=None), NULL),
+    (dict(B=0), SHAPE), (dict(qsl=0), SHAPE), (dict(ksl=-1), SHAPE), (dict(n_qh=0), SHAPE),
+    (dict(n_kvh=0), SHAPE), (dict(n_qh=6, n_kvh=4), SHAPE),
+    (dict(causal=1, qsl=65, ksl=64), SHAPE),
+    (dict(cu=FAKE, qsl=64, ksl=63), SHAPE),
+    (dict(hdim=96), UNSUP), (dict(hdim=256), UNSUP), (dict(cu=FAKE, route=FAKE), UNSUP),
+    (dict(scale=float("nan")), ARG), (dict(scale=float("inf")), ARG), (dict(scale=0.0), ARG),
+    (dict(route=FAKE, tpb=0), ARG),
+    (dict(q=FAKE + 8), ARG), (dict(out=FAKE + 2), ARG), (dict(route=FAKE + 2), ARG),
+])
+def test_validation_codes(kw, code):
+    assert call(**kw) == code
+    assert A.attn_last_error() != ""
+
+
+def test_error_message_names_the_problem():
+    assert call(hdim=80) == UNSUP
+    assert "hdim" in A.attn_last_error()
+    assert call(n_qh=5, n_kvh=2) == SHAPE
+    assert "multiple" in A.attn_last_error()
+
+
+def test_debug_hooks_validate():
+    lib = A.load()
+    assert lib.attn_debug_quantize_rows(None, 4, 64, FAKE, FAKE, 0, None) == NULL
+    assert lib.attn_debug_quantize_rows(FAKE, 4, 96, FAKE, FAKE, 0, None) == UNSUP
+    assert lib.attn_debug_quantize_rows(FAKE, 4, 64, FAKE, FAKE, 7, None) == ARG
+    assert lib.attn_debug_route_dump(FAKE, 64, 64, 0, 4, None, None) == NULL
+    assert lib.attn_debug_route_dump(FAKE, 65, 64, 1, 4, FAKE, None) == SHAPE
+    assert lib.attn_debug_route_dump(FAKE, 64, 64, 0, 0, FAKE, None) == ARG
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        A.attn_fwd(q, q, q)
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "attention_prefill_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

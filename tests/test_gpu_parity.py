@@ -1,0 +1,352 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Tolerance on fp16 outputs for N(0,1) inputs: max abs error <= 4e-3 and mean
+abs error <= 5e-4.  Integer work (INT8 codes, routing decode) is compared
+bit-exactly.  Small cases span several tiles with ragged tails; the
+full-size workloads are run in the launch configuration bench.py times and
+checked on sampled rows the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+MAX_ERR = 4e-3
+MEAN_ERR = 5e-4
+
+
+@pytest.fixture(scope="module")
+def A():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_prefill_amd as A
+    A.load()
+    return A
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def words_tensor(route):
+    return None if route is None else dev(np.ascontiguousarray(route, dtype=np.uint32).view(np.int32))
+
+
+def gpu_attn(A, q, k, v, scale, causal, cu=None, route=None, tpb=4):
+    out = A.attn_fwd(dev(q), dev(k), dev(v), scale=scale, causal=causal,
+                     cu_seqlens=None if cu is None else dev(np.asarray(cu, dtype=np.int32)),
+                     route_bitmask=words_tensor(route), tiles_per_bit=tpb)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(got, ref, label=""):
+    g = got.astype(np.float64)
+    assert np.all(np.isfinite(g)), label
+    err = np.abs(g - ref)
+    assert err.max() <= MAX_ERR and err.mean() <= MEAN_ERR, \
+        "%s max %.3g mean %.3g" % (label, err.max(), err.mean())
+    return err.max(), err.mean()
+
+
+def rand16(rng, shape):
+    return rng.standard_normal(shape).astype(np.float16)
+
+
+# --------------------------------------------------------------------------
+# small and ragged shapes vs the full oracle
+# --------------------------------------------------------------------------
+
+SHAPES = [(1, 1), (5, 70), (64, 64), (65, 65), (130, 130), (200, 333), (333, 200), (300, 1000)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("heads", [(3, 3), (4, 2), (8, 2), (8, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_ragged(A, orc, d, heads, causal):
+    rng = np.random.default_rng(d * 100 + heads[0] * 10 + heads[1] + causal)
+    for (qsl, ksl) in SHAPES:
+        if causal and qsl > ksl:
+            continue
+        B = 2 if qsl <= 70 else 1
+        say("dense d=%d heads=%s causal=%d B=%d qsl=%d ksl=%d" % (d, heads, causal, B, qsl, ksl))
+        q, k, v = rand16(rng, (B, heads[0], qsl, d)), rand16(rng, (B, heads[1], ksl, d)), \
+            rand16(rng, (B, heads[1], ksl, d))
+        scale = float(np.float32(1 / np.sqrt(d)))
+        got = gpu_attn(A, q, k, v, scale, causal)
+        ref = orc.attn_fwd(q, k, v, scale=scale, causal=causal)
+        check(got, ref, (qsl, ksl))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("heads", [(2, 2), (8, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_ragged(A, orc, d, heads, causal):
+    rng = np.random.default_rng(7 + d + heads[1] + causal)
+    lens = [1, 63, 64, 65, 200, 0, 130, 7]
+    cu = W.cu_seqlens_of(lens)
+    T = int(cu[-1])
+    say("varlen d=%d heads=%s causal=%d lens=%s" % (d, heads, causal, lens))
+    q, k, v = rand16(rng, (heads[0], T, d)), rand16(rng, (heads[1], T, d)), rand16(rng, (heads[1], T, d))
+    got = gpu_attn(A, q, k, v, 0.1, causal, cu=cu)
+    ref = orc.attn_fwd(q, k, v, scale=0.1, causal=causal, cu_seqlens=cu)
+    check(got, ref)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("heads", [(2, 2), (4, 2), (8, 2), (12, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tpb", [1, 3, 4])
+def test_routed_ragged(A, orc, d, heads, causal, tpb):
+    rng = np.random.default_rng(3 * d + heads[0] + 5 * heads[1] + causal + 11 * tpb)
+    for (qsl, ksl) in [(64, 64), (130, 130), (200, 700), (333, 200)]:
+        if causal and qsl > ksl:
+            continue
+        say("routed d=%d heads=%s causal=%d tpb=%d qsl=%d ksl=%d" % (d, heads, causal, tpb, qsl, ksl))
+        q, k, v = rand16(rng, (1, heads[0], qsl, d)), rand16(rng, (1, heads[1], ksl, d)), \
+            rand16(rng, (1, heads[1], ksl, d))
+        route = W.draw_route(qsl, ksl, tpb, 0.5, seed=int(rng.integers(1 << 30)))
+        scale = float(np.float32(1 / np.sqrt(d)))
+        got = gpu_attn(A, q, k, v, scale, causal, route=route, tpb=tpb)
+        ref = orc.attn_fwd(q, k, v, scale=scale, causal=causal, route=route, tiles_per_bit=tpb)
+        check(got, ref, (qsl, ksl))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_routed_all_int8(A, orc, d):
+    rng = np.random.default_rng(40 + d)
+    qsl = ksl = 300
+    q, k, v = rand16(rng, (1, 4, qsl, d)), rand16(rng, (1, 1, ksl, d)), rand16(rng, (1, 1, ksl, d))
+    route = W.pack_bits(np.ones((5, 5), dtype=bool))
+    say("all-int8 d=%d" % d)
+    for causal in (False, True):
+        got = gpu_attn(A, q, k, v, 0.1, causal, route=route, tpb=1)
+        ref = orc.attn_fwd(q, k, v, scale=0.1, causal=causal, route=route, tiles_per_bit=1)
+        check(got, ref)
+
+
+def test_negative_scale(A, orc):
+    rng = np.random.default_rng(50)
+    q, k, v = rand16(rng, (1, 4, 100, 64)), rand16(rng, (1, 2, 150, 64)), rand16(rng, (1, 2, 150, 64))
+    route = W.pack_bits(rng.random((2, 3)) < 0.5)
+    say("negative scale")
+    for r in (None, route):
+        got = gpu_attn(A, q, k, v, -0.125, True, route=r, tpb=1)
+        ref = orc.attn_fwd(q, k, v, scale=-0.125, causal=True, route=r, tiles_per_bit=1)
+        check(got, ref)
+
+
+# --------------------------------------------------------------------------
+# invariants on the GPU
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("routed", [False, True])
+def test_gpu_causal_row0_is_v0(A, routed):
+    rng = np.random.default_rng(60)
+    q, k, v = rand16(rng, (1, 8, 200, 128)), rand16(rng, (1, 2, 200, 128)), rand16(rng, (1, 2, 200, 128))
+    route = W.pack_bits(np.ones((4, 1), dtype=bool)) if routed else None
+    got = gpu_attn(A, q, k, v, 0.088388346, True, route=route, tpb=4)
+    for h in range(8):
+        assert np.array_equal(got[0, h, 0], v[0, h // 4, 0])
+
+
+@pytest.mark.parametrize("routed", [False, True])
+def test_gpu_equal_scores_give_mean(A, routed):
+    rng = np.random.default_rng(61)
+    q = np.zeros((1, 4, 70, 64), dtype=np.float16)
+    k, v = rand16(rng, (1, 4, 250, 64)), rand16(rng, (1, 4, 250, 64))
+    route = W.pack_bits(np.ones((2, 4), dtype=bool)) if routed else None
+    got = gpu_attn(A, q, k, v, 0.125, False, route=route, tpb=1)
+    mean = v.astype(np.float64).mean(axis=2)
+    assert np.max(np.abs(got.astype(np.float64) - mean[:, :, None, :])) <= 1e-3
+
+
+@pytest.mark.parametrize("routed", [False, True])
+def test_gpu_rows_sum_to_one(A, routed):
+    rng = np.random.default_rng(62)
+    q, k, v = rand16(rng, (1, 4, 190, 128)), rand16(rng, (1, 1, 400, 128)), rand16(rng, (1, 1, 400, 128))
+    v[..., 0] = 1.0
+    route = W.pack_bits(rng.random((3, 7)) < 0.5) if routed else None
+    for causal in (False, True):
+        got = gpu_attn(A, q, k, v, 0.09, causal, route=route, tpb=1)
+        assert np.max(np.abs(got[..., 0].astype(np.float64) - 1.0)) <= 2e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_gpu_all_zero_mask_is_dense_bitexact(A, d):
+    rng = np.random.default_rng(63)
+    q, k, v = rand16(rng, (1, 8, 300, d)), rand16(rng, (1, 2, 300, d)), rand16(rng, (1, 2, 300, d))
+    zeros = W.pack_bits(np.zeros((5, 2), dtype=bool))
+    for causal in (False, True):
+        a = gpu_attn(A, q, k, v, 0.1, causal, route=zeros, tpb=4)
+        b = gpu_attn(A, q, k, v, 0.1, causal)
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_gpu_varlen_equals_separate_calls(A):
+    rng = np.random.default_rng(64)
+    lens = [70, 1, 129, 300]
+    cu = W.cu_seqlens_of(lens)
+    T = int(cu[-1])
+    q, k, v = rand16(rng, (8, T, 128)), rand16(rng, (2, T, 128)), rand16(rng, (2, T, 128))
+    packed = gpu_attn(A, q, k, v, 0.1, True, cu=cu)
+    for s in range(len(lens)):
+        a, b = cu[s], cu[s + 1]
+        one = gpu_attn(A, q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], 0.1, True)
+        assert np.array_equal(packed[:, a:b].view(np.uint16), one[0].view(np.uint16))
+
+
+def test_gpu_bottom_right_is_tail_of_full(A):
+    rng = np.random.default_rng(65)
+    ksl = 600
+    q, k, v = rand16(rng, (1, 4, ksl, 128)), rand16(rng, (1, 1, ksl, 128)), rand16(rng, (1, 1, ksl, 128))
+    full = gpu_attn(A, q, k, v, 0.1, True)
+    for qsl in (1, 100, 128, 333):
+        tail = gpu_attn(A, q[:, :, ksl - qsl:], k, v, 0.1, True)
+        err = np.abs(tail.astype(np.float64) - full[:, :, ksl - qsl:].astype(np.float64))
+        assert err.max() <= 2e-3
+
+
+@pytest.mark.parametrize("routed", [False, True])
+@pytest.mark.parametrize("kexp", [-1, 2])
+def test_gpu_power_of_two_scale_equivariance(A, routed, kexp):
+    rng = np.random.default_rng(66)
+    q, k, v = rand16(rng, (1, 4, 150, 64)), rand16(rng, (1, 2, 230, 64)), rand16(rng, (1, 2, 230, 64))
+    route = W.pack_bits(rng.random((3, 4)) < 0.5) if routed else None
+    a = gpu_attn(A, q, k, v, 0.125, True, route=route, tpb=1)
+    q2 = (q.astype(np.float64) * 2.0 ** kexp).astype(np.float16)
+    b = gpu_attn(A, q2, k, v, 0.125 * 2.0 ** -kexp, True, route=route, tpb=1)
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# INT8 codes and routing decode, bit-exact
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("path", [0, 1])
+def test_gpu_quantizer_bitexact(A, orc, d, path):
+    rng = np.random.default_rng(70 + d + path)
+    rows = np.concatenate([
+        rand16(rng, (200, d)),
+        (rng.standard_normal((50, d)) * 1e-3).astype(np.float16),
+        (rng.standard_normal((50, d)) * 3e3).astype(np.float16),
+        np.zeros((3, d), dtype=np.float16),
+    ])
+    # rows whose codes sit on exact ties: amax 127 (inv 1) with half-integers
+    tie = np.zeros((4, d), dtype=np.float16)
+    tie[:, 0] = 127
+    tie[:, 1:] = (np.arange(1, d) % 40 - 20 + 0.5).astype(np.float16)
+    rows = np.ascontiguousarray(np.concatenate([rows, tie]))
+    say("quantizer d=%d path=%d rows=%d" % (d, path, rows.shape[0]))
+    q8, s = A.attn_debug_quantize_rows(dev(rows), path=path)
+    q8, s = q8.cpu().numpy(), s.cpu().numpy()
+    for r in range(rows.shape[0]):
+        rq, rs = orc.quantize_row(rows[r])
+        assert np.array_equal(q8[r], rq), r
+        assert s[r] == rs, r
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gpu_route_dump_bitexact(A, orc, causal):
+    rng = np.random.default_rng(80 + causal)
+    for (qsl, ksl, tpb) in [(16384, 16384, 4), (512, 4096, 4), (100, 4000, 3), (64, 64, 1), (2100, 2100, 2)]:
+        if causal and qsl > ksl:
+            continue
+        n_qt, n_kt = -(-qsl // 64), -(-ksl // 64)
+        n_g = -(-n_kt // tpb)
+        bits = rng.random((n_qt, n_g)) < 0.5
+        words = W.pack_bits(bits)
+        got = A.attn_debug_route_dump(words_tensor(words), qsl, ksl, causal, tpb).cpu().numpy()
+        wpr = words.shape[1]
+        off = ksl - qsl
+        exp = np.zeros((n_qt, n_kt), dtype=np.uint8)
+        for qt in range(n_qt):
+            last = min(qt * 64 + 64, qsl) - 1
+            for kt in range(n_kt):
+                if causal and kt * 64 > last + off:
+                    exp[qt, kt] = 2
+                else:
+                    exp[qt, kt] = orc.route_bit(words, wpr, qt, kt // tpb)
+        assert np.array_equal(got, exp), (qsl, ksl, tpb)
+
+
+def test_gpu_single_bit_flip_changes_only_its_qtile(A, orc):
+    """Adversarial K (one large entry per row) makes INT8 scores differ from FP16
+    by far more than the tolerance, so every routed bit is visible."""
+    rng = np.random.default_rng(90)
+    qsl = ksl = 256
+    q = rand16(rng, (1, 4, qsl, 64))
+    k = (rng.standard_normal((1, 1, ksl, 64)) * 0.05).astype(np.float16)
+    k[..., 0] = 60.0
+    v = rand16(rng, (1, 1, ksl, 64))
+    base_bits = np.zeros((4, 4), dtype=bool)
+    base = gpu_attn(A, q, k, v, 0.125, False, route=W.pack_bits(base_bits), tpb=1)
+    for (qt, g) in [(0, 0), (1, 3), (3, 2)]:
+        bits = base_bits.copy()
+        bits[qt, g] = True
+        got = gpu_attn(A, q, k, v, 0.125, False, route=W.pack_bits(bits), tpb=1)
+        changed = np.nonzero(np.any(got != base, axis=(0, 1, 3)))[0]
+        assert changed.size > 0 and changed.min() >= 64 * qt and changed.max() < 64 * (qt + 1)
+        ref = orc.attn_fwd(q, k, v, scale=0.125, causal=False, route=W.pack_bits(bits), tiles_per_bit=1)
+        check(got, ref)
+
+
+# --------------------------------------------------------------------------
+# the measured workloads at full size
+# --------------------------------------------------------------------------
+
+
+def sample_rows(rng, w, n_per_head):
+    rows = []
+    if w.varlen:
+        for h in range(w.n_qh):
+            for s, L in enumerate(w.seqlens):
+                pick = {0, L - 1} | set(rng.integers(0, L, n_per_head).tolist())
+                rows += [(s, h, int(i)) for i in sorted(pick)]
+    else:
+        for b in range(w.B):
+            for h in range(w.n_qh):
+                pick = {0, w.qsl - 1} | set(rng.integers(0, w.qsl, n_per_head).tolist())
+                rows += [(b, h, int(i)) for i in sorted(pick)]
+    return rows
+
+
+def gather(out, rows, varlen, cu):
+    if varlen:
+        return np.stack([out[h, cu[s] + i] for (s, h, i) in rows])
+    return np.stack([out[b, h, i] for (b, h, i) in rows])
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_workload_full_size(A, orc, name):
+    w = W.WORKLOADS[name]
+    say("workload", name)
+    q, k, v = W.draw_qkv(w)
+    route = W.route_for(w)
+    cu = W.cu_seqlens_of(w.seqlens) if w.varlen else None
+    got = gpu_attn(A, q, k, v, w.scale, w.causal, cu=cu, route=route, tpb=w.tiles_per_bit or 4)
+    rng = np.random.default_rng(1234)
+    if w.qsl * w.ksl * w.n_qh <= 256 * 256 * 4:
+        ref = orc.attn_fwd(q, k, v, scale=w.scale, causal=w.causal, cu_seqlens=cu, route=route,
+                           tiles_per_bit=w.tiles_per_bit or 4)
+        check(got, ref, name)
+        return
+    rows = sample_rows(rng, w, 6 if w.qsl <= 4096 else 3)
+    ref = orc.attn_rows(q, k, v, rows, scale=w.scale, causal=w.causal, cu_seqlens=cu, route=route,
+                        tiles_per_bit=w.tiles_per_bit or 4)
+    mx, mn = check(gather(got, rows, w.varlen, cu), ref, name)
+    say("  rows %d max %.3g mean %.3g" % (len(rows), mx, mn))
+    assert np.all(np.isfinite(got.astype(np.float32)))
