@@ -37,6 +37,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "attn_internal.h"
 
 namespace attn {
@@ -49,11 +51,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 64;          // keys per tile
 constexpr int TQ = 64;          // query rows per routing tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23
+// dword 3 of a raw buffer descriptor (32-bit data format, no swizzle, no
+// index stride): reads beyond num_records return zero.
+constexpr int BUF_DWORD3 = 0x00020000;
 
 // ---------------------------------------------------------------------------
 // INT8 quantisation rule shared by the K pass, the query prologue and the
@@ -133,19 +140,21 @@ __device__ __forceinline__ bool route_bit(const uint32_t* row, int kt, int tiles
 }
 
 // ---------------------------------------------------------------------------
-// LDS layout of one stage: K tile (fp16, or INT8 codes + scaled s_k) then V.
-// Row pitches are padded so that the row-parallel reads of the MFMA operands
-// spread over the banks.
+// LDS layout of one stage: the K tile (fp16 [key][d], or INT8 codes [key][d]
+// followed by the 64 scaled K scales) and the V tile stored transposed,
+// [d][key], so that the P.V operand (8 consecutive keys of one d) is a single
+// 16-byte read.  Row pitches are padded so that the row-parallel operand
+// reads and the staging writes spread over the banks.
 // ---------------------------------------------------------------------------
 template <int HD>
 struct Lds {
     static constexpr int KP = HD + 8;            // fp16 elements per K row
-    static constexpr int VP = HD + 16;           // fp16 elements per V row
+    static constexpr int VTP = BN + 8;           // fp16 elements per V^T row
     static constexpr int K8P = HD + 16;          // bytes per INT8 K row
     static constexpr int KBYTES = BN * KP * 2;
     static constexpr int K8BYTES = BN * K8P + BN * 4;
     static constexpr int KREG = KBYTES > K8BYTES ? KBYTES : K8BYTES;
-    static constexpr int VBYTES = BN * VP * 2;
+    static constexpr int VBYTES = HD * VTP * 2;
     static constexpr int STAGE = KREG + VBYTES;
     static constexpr int TOTAL = 2 * STAGE;
 };
@@ -167,6 +176,14 @@ struct FwdArgs {
     int neg;                // scale < 0: queries are negated
 };
 
+// Running max starts finite so that no exp2 argument is ever (-inf) - (-inf).
+constexpr float M_INIT = -1.0e30f;
+// The reference max of a row moves only when a new score exceeds it by more
+// than TAU (log2 units); until then exp2(x - m) <= 2^TAU, which fp16 P and
+// the fp32 sums hold exactly as well as values <= 1.  The result O / l does
+// not depend on the reference chosen.
+constexpr float TAU = 8.0f;
+
 // ---------------------------------------------------------------------------
 // Fused forward kernel.
 // ---------------------------------------------------------------------------
@@ -174,9 +191,11 @@ template <int HD, int NW, bool CAUSAL, bool VARLEN, bool ROUTED>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     using L = Lds<HD>;
     constexpr int NT = NW * 64;
-    constexpr int KCH = BN * HD / 8 / NT;      // 16-byte fp16 chunks per thread (K or V)
-    constexpr int K8CH = BN * HD / 16 / NT;    // 16-byte INT8 chunks per thread
-    constexpr int NDB = HD / 32;               // 32-row blocks of d in O^T
+    constexpr int KCH = BN * HD / 8 / NT;              // 16-byte fp16 K chunks per thread
+    constexpr int K8CH = BN * HD / 16 / NT;            // 16-byte INT8 K chunks per thread
+    constexpr int VBLK = (BN / 4) * (HD / 8);          // 4-key x 8-d V blocks per tile
+    constexpr int VB = (VBLK + NT - 1) / NT;           // V blocks per thread
+    constexpr int NDB = HD / 32;                       // 32-row blocks of d in O^T
     static_assert(KCH >= 1 && K8CH >= 1, "tile too small for the workgroup");
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -242,24 +261,24 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     const uint32_t* rrow = ROUTED ? a.route + (size_t)(m0 / TQ) * a.wpr : nullptr;
 
     // ---- query rows into the score B-operand layout ---------------------------
+    const int qi = r0 + lq;
     f16x8 qf[HD / 16];
     {
-        const int qi = r0 + lq;
-        const _Float16* qp = qb + (size_t)qi * HD + 16 * g;
+        // rows past the end read the last row (finite values, never stored)
+        const _Float16* qp = qb + (size_t)min(qi, Lq - 1) * HD + 16 * g;
 #pragma unroll
         for (int kb2 = 0; kb2 < HD / 32; ++kb2) {
-            if (qi < Lq) {
-                qf[2 * kb2] = *(const f16x8*)(qp + 32 * kb2);
-                qf[2 * kb2 + 1] = *(const f16x8*)(qp + 32 * kb2 + 8);
-            } else {
-                qf[2 * kb2] = f16x8{};
-                qf[2 * kb2 + 1] = f16x8{};
-            }
+            qf[2 * kb2] = *(const f16x8*)(qp + 32 * kb2);
+            qf[2 * kb2 + 1] = *(const f16x8*)(qp + 32 * kb2 + 8);
         }
         if (a.neg) {
 #pragma unroll
             for (int t = 0; t < HD / 16; ++t) qf[t] = -qf[t];
         }
+        // Settle the query loads here: otherwise the wait-count analysis at the
+        // loop header cannot tell them from the tile prefetches and makes every
+        // score MFMA wait for the next tile's loads.
+        __builtin_amdgcn_s_waitcnt(0);
     }
     i32x4 q8[ROUTED ? HD / 32 : 1];
     float sq_mul = 1.0f;
@@ -270,61 +289,73 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     }
 
     // ---- tile loader ------------------------------------------------------------
-    uint4 kreg[KCH], vreg[KCH];
-    float skreg[4];
+    // K: 16-byte chunks of rows.  V: per thread a block of 4 keys x 8 d, read as
+    // four 16-byte row pieces and written transposed as eight 8-byte pieces.
+    // Loads go through buffer descriptors covering exactly this sequence's
+    // rows: reads past the last key return zeros (those keys are masked to
+    // -inf, so P is exactly 0 there), the per-lane offsets are loop
+    // invariant and the tile advance is a scalar offset, so nothing in the
+    // loop waits on the loads of the next tile before its LDS store.
+    const int slab = Lk * HD * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, slab, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, slab, BUF_DWORD3);
+    __amdgpu_buffer_rsrc_t k8rs = krs, skrs = krs;
+    if constexpr (ROUTED) {
+        k8rs = __builtin_amdgcn_make_buffer_rsrc((void*)k8b, (short)0, Lk * HD, BUF_DWORD3);
+        skrs = __builtin_amdgcn_make_buffer_rsrc((void*)skb, (short)0, Lk * 4, BUF_DWORD3);
+    }
+    u32x4 kreg[KCH];
+    u32x4 vreg[VB][4];
+    u32x4 skreg;
 
-    auto gload = [&](int kt, bool i8) {
-        const int key0 = kt * BN;
+    auto gload = [&](int kt, bool i8) __attribute__((always_inline)) {
         if (ROUTED && i8) {
+            const int soff = kt * BN * HD;
 #pragma unroll
             for (int n = 0; n < K8CH; ++n) {
-                const int c = tid + n * NT;
-                const int row = c / (HD / 16);
-                const int col = (c % (HD / 16)) * 16;
-                const int key = key0 + row;
-                kreg[n] = key < Lk ? *(const uint4*)(k8b + (size_t)key * HD + col) : uint4{0, 0, 0, 0};
+                const int c = tid + n * NT;     // row c / (HD/16), 16-byte column c % (HD/16)
+                kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k8rs, c * 16, soff, 0));
             }
-            if (tid < BN / 4) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = key0 + 4 * tid + e;
-                    skreg[e] = key < Lk ? skb[key] : 0.0f;
-                }
-            }
+            if (tid < BN / 4)
+                skreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(skrs, tid * 16, kt * BN * 4, 0));
         } else {
+            const int soff = kt * BN * HD * 2;
 #pragma unroll
             for (int n = 0; n < KCH; ++n) {
-                const int c = tid + n * NT;
-                const int row = c / (HD / 8);
-                const int col = (c % (HD / 8)) * 8;
-                const int key = key0 + row;
-                kreg[n] = key < Lk ? *(const uint4*)(kb + (size_t)key * HD + col) : uint4{0, 0, 0, 0};
+                const int c = tid + n * NT;     // row c / (HD/8), 16-byte column c % (HD/8)
+                kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, c * 16, soff, 0));
             }
         }
+        const int soff = kt * BN * HD * 2;
 #pragma unroll
-        for (int n = 0; n < KCH; ++n) {
-            const int c = tid + n * NT;
-            const int row = c / (HD / 8);
-            const int col = (c % (HD / 8)) * 8;
-            const int key = key0 + row;
-            vreg[n] = key < Lk ? *(const uint4*)(vb + (size_t)key * HD + col) : uint4{0, 0, 0, 0};
+        for (int n = 0; n < VB; ++n) {
+            const int bi = tid + n * NT;
+            if (VBLK % NT == 0 || bi < VBLK) {
+                const int kg = bi % (BN / 4);
+                const int dc = bi / (BN / 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vreg[n][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                        vrs, ((4 * kg + i) * HD + 8 * dc) * 2, soff, 0));
+            }
         }
     };
 
-    auto lstore = [&](int stage, bool i8) {
+    auto lstore = [&](int stage, bool i8) __attribute__((always_inline)) {
         char* kbuf = smem + stage * L::STAGE;
-        _Float16* vbuf = (_Float16*)(kbuf + L::KREG);
+        _Float16* vt = (_Float16*)(kbuf + L::KREG);
         if (ROUTED && i8) {
 #pragma unroll
             for (int n = 0; n < K8CH; ++n) {
                 const int c = tid + n * NT;
                 const int row = c / (HD / 16);
                 const int col = (c % (HD / 16)) * 16;
-                *(uint4*)(kbuf + row * L::K8P + col) = kreg[n];
+                *(u32x4*)(kbuf + row * L::K8P + col) = kreg[n];
             }
             if (tid < BN / 4) {
                 float* skc = (float*)(kbuf + BN * L::K8P);
-                *(f32x4*)(skc + 4 * tid) = f32x4{skreg[0] * a.c, skreg[1] * a.c, skreg[2] * a.c, skreg[3] * a.c};
+                const f32x4 sv = __builtin_bit_cast(f32x4, skreg);
+                *(f32x4*)(skc + 4 * tid) = sv * a.c;
             }
         } else {
             _Float16* k16 = (_Float16*)kbuf;
@@ -333,15 +364,28 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
                 const int c = tid + n * NT;
                 const int row = c / (HD / 8);
                 const int col = (c % (HD / 8)) * 8;
-                *(uint4*)(k16 + row * L::KP + col) = kreg[n];
+                *(u32x4*)(k16 + row * L::KP + col) = kreg[n];
             }
         }
 #pragma unroll
-        for (int n = 0; n < KCH; ++n) {
-            const int c = tid + n * NT;
-            const int row = c / (HD / 8);
-            const int col = (c % (HD / 8)) * 8;
-            *(uint4*)(vbuf + row * L::VP + col) = vreg[n];
+        for (int n = 0; n < VB; ++n) {
+            const int bi = tid + n * NT;
+            if (VBLK % NT == 0 || bi < VBLK) {
+                const int kg = bi % (BN / 4);
+                const int dc = bi / (BN / 4);
+                const u32x4 r0w = vreg[n][0], r1w = vreg[n][1], r2w = vreg[n][2], r3w = vreg[n][3];
+                _Float16* dst = vt + (8 * dc) * L::VTP + 4 * kg;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // d = 8*dc + 2j takes the low halves, d + 1 the high halves
+                    *(u32x2*)(dst + (2 * j) * L::VTP) =
+                        u32x2{__builtin_amdgcn_perm(r1w[j], r0w[j], 0x05040100u),
+                              __builtin_amdgcn_perm(r3w[j], r2w[j], 0x05040100u)};
+                    *(u32x2*)(dst + (2 * j + 1) * L::VTP) =
+                        u32x2{__builtin_amdgcn_perm(r1w[j], r0w[j], 0x07060302u),
+                              __builtin_amdgcn_perm(r3w[j], r2w[j], 0x07060302u)};
+                }
+            }
         }
     };
 
@@ -349,12 +393,118 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    float m_run = -INFINITY;
+    float m_run = M_INIT;
     float l_run = 0.0f;
 
     // K row read by this lane for the score A operand: bits 2 and 3 swapped
     const int krow = (lq & ~12) | ((lq & 4) << 1) | ((lq & 8) >> 1);
-    const int qi = r0 + lq;
+
+    // One key tile: scores, optional mask, online softmax, P.V.
+    auto tile = [&](auto mask_tag, int kt, bool i8) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const char* kbuf = smem + (kt & 1) * L::STAGE;
+        const _Float16* vt = (const _Float16*)(kbuf + L::KREG);
+        float x[2][16];
+        float amul;
+        if (ROUTED && i8) {
+            const float* skc = (const float*)(kbuf + BN * L::K8P);
+#pragma unroll
+            for (int kb32 = 0; kb32 < 2; ++kb32) {
+                i32x16 acc = i32x16{};
+                const int8_t* kr = (const int8_t*)kbuf + (32 * kb32 + krow) * L::K8P + 16 * g;
+#pragma unroll
+                for (int ks = 0; ks < HD / 32; ++ks) {
+                    i32x4 av = *(const i32x4*)(kr + 32 * ks);
+                    acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, q8[ks], acc, 0, 0, 0);
+                }
+                // this lane's keys: 32*kb32 + 8*g + (i%8) + 16*(i/8)
+                const float* sp = skc + 32 * kb32 + 8 * g;
+                const f32x4 s0 = *(const f32x4*)(sp);
+                const f32x4 s1 = *(const f32x4*)(sp + 4);
+                const f32x4 s2 = *(const f32x4*)(sp + 16);
+                const f32x4 s3 = *(const f32x4*)(sp + 20);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[kb32][i] = (float)acc[i] * s0[i];
+                    x[kb32][4 + i] = (float)acc[4 + i] * s1[i];
+                    x[kb32][8 + i] = (float)acc[8 + i] * s2[i];
+                    x[kb32][12 + i] = (float)acc[12 + i] * s3[i];
+                }
+            }
+            amul = sq_mul;
+        } else {
+            const _Float16* k16 = (const _Float16*)kbuf;
+#pragma unroll
+            for (int kb32 = 0; kb32 < 2; ++kb32) {
+                f32x16 acc = f32x16{};
+                const _Float16* kr = k16 + (32 * kb32 + krow) * L::KP + 16 * g;
+#pragma unroll
+                for (int t = 0; t < HD / 16; ++t) {
+                    const f16x8 av = *(const f16x8*)(kr + 32 * (t / 2) + 8 * (t % 2));
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[t], acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) x[kb32][i] = acc[i];
+            }
+            amul = a.c;
+        }
+
+        if constexpr (MASK) {
+            // keys past the end and the bottom-right causal boundary
+            const int lim = CAUSAL ? min(Lk - 1, qi + off) : Lk - 1;
+            const int kl = kt * BN + 8 * g;
+#pragma unroll
+            for (int kb32 = 0; kb32 < 2; ++kb32)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (kl + 32 * kb32 + (i % 8) + 16 * (i / 8) > lim) x[kb32][i] = -INFINITY;
+        }
+
+        // online softmax in base 2 with a lazily moved reference max
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb32 = 0; kb32 < 2; ++kb32)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, x[kb32][i]);
+        mt = halfwave_max(mt) * amul;
+        if (__any(mt > m_run + TAU)) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        }
+        const float nm = -m_run;
+        f16x8 pk[2][2];
+        float rs = 0.0f;
+#pragma unroll
+        for (int kb32 = 0; kb32 < 2; ++kb32)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb32][8 * t + j], amul, nm));
+                    rs += p;
+                    pk[kb32][t][j] = (_Float16)p;
+                }
+        l_run += rs;
+
+        // O^T += V^T P^T over the four 16-key steps of the tile
+        const _Float16* vrow = vt + lq * L::VTP + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const f16x8 av = *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[kk >> 1][kk & 1], o[db], 0, 0, 0);
+            }
+    };
+
+    // Tiles [0, nfull) are fully visible to every row of the workgroup; the
+    // rest (the causal diagonal and a partial last tile) go through the
+    // masked variant.  Two loops keep the two variants' live ranges apart.
+    const int nfull = min(nkt, min(Lk / BN, CAUSAL ? (m0 + off + 1) / BN : nkt));
 
     bool i8_next = ROUTED && nkt > 0 && route_bit(rrow, 0, a.tiles_per_bit);
     if (nkt > 0) {
@@ -363,126 +513,22 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     }
     __syncthreads();
 
-    for (int kt = 0; kt < nkt; ++kt) {
+    int kt = 0;
+    for (; kt < nfull; ++kt) {
         const bool i8_cur = i8_next;
         const bool more = kt + 1 < nkt;
         i8_next = ROUTED && more && route_bit(rrow, kt + 1, a.tiles_per_bit);
         if (more) gload(kt + 1, i8_next);
-
-        if (kt < w_nkt) {
-            const char* kbuf = smem + (kt & 1) * L::STAGE;
-            const _Float16* vbuf = (const _Float16*)(kbuf + L::KREG);
-            float x[2][16];
-            float amul;
-            // -- scores S^T = K Q^T for the two 32-key blocks of the tile
-            if (ROUTED && i8_cur) {
-                const float* skc = (const float*)(kbuf + BN * L::K8P);
-#pragma unroll
-                for (int kb32 = 0; kb32 < 2; ++kb32) {
-                    i32x16 acc = i32x16{};
-                    const int8_t* kr = (const int8_t*)kbuf + (32 * kb32 + krow) * L::K8P + 16 * g;
-#pragma unroll
-                    for (int ks = 0; ks < HD / 32; ++ks) {
-                        i32x4 av = *(const i32x4*)(kr + 32 * ks);
-                        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, q8[ks], acc, 0, 0, 0);
-                    }
-                    // lane's keys: 32*kb32 + 8*g + (i%8) + 16*(i/8)
-                    const float* sp = skc + 32 * kb32 + 8 * g;
-                    f32x4 s0 = *(const f32x4*)(sp);
-                    f32x4 s1 = *(const f32x4*)(sp + 4);
-                    f32x4 s2 = *(const f32x4*)(sp + 16);
-                    f32x4 s3 = *(const f32x4*)(sp + 20);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        x[kb32][i] = (float)acc[i] * s0[i];
-                        x[kb32][4 + i] = (float)acc[4 + i] * s1[i];
-                        x[kb32][8 + i] = (float)acc[8 + i] * s2[i];
-                        x[kb32][12 + i] = (float)acc[12 + i] * s3[i];
-                    }
-                }
-                amul = sq_mul;
-            } else {
-                const _Float16* k16 = (const _Float16*)kbuf;
-#pragma unroll
-                for (int kb32 = 0; kb32 < 2; ++kb32) {
-                    f32x16 acc = f32x16{};
-                    const _Float16* kr = k16 + (32 * kb32 + krow) * L::KP + 16 * g;
-#pragma unroll
-                    for (int t = 0; t < HD / 16; ++t) {
-                        f16x8 av = *(const f16x8*)(kr + 32 * (t / 2) + 8 * (t % 2));
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[t], acc, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) x[kb32][i] = acc[i];
-                }
-                amul = a.c;
-            }
-
-            // -- mask: keys past the end, and the bottom-right causal boundary
-            const int key0 = kt * BN;
-            const bool need_mask = (key0 + BN > Lk) || (CAUSAL && key0 + BN - 1 > r0 + off);
-            if (need_mask) {
-                const int lim = CAUSAL ? min(Lk - 1, qi + off) : Lk - 1;
-#pragma unroll
-                for (int kb32 = 0; kb32 < 2; ++kb32)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + 32 * kb32 + 8 * g + (i % 8) + 16 * (i / 8);
-                        if (key > lim) x[kb32][i] = -INFINITY;
-                    }
-            }
-
-            // -- online softmax (base 2)
-            float mt = -INFINITY;
-#pragma unroll
-            for (int kb32 = 0; kb32 < 2; ++kb32)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mt = fmaxf(mt, x[kb32][i]);
-            mt = halfwave_max(mt);
-            const float m_new = fmaxf(m_run, mt * amul);
-            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
-
-            f16x8 pk[2][2];
-            float rs = 0.0f;
-#pragma unroll
-            for (int kb32 = 0; kb32 < 2; ++kb32)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb32][8 * t + j], amul, -m_use));
-                        rs += p;
-                        pk[kb32][t][j] = (_Float16)p;
-                    }
-            l_run = l_run * alpha + rs;
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-            }
-
-            // -- O^T += V^T P^T
-            const int vr = 8 * g + ((l & 15) >> 2);
-            const int vc = 16 * ((l >> 4) & 1) + 4 * (l & 3);
-#pragma unroll
-            for (int kb32 = 0; kb32 < 2; ++kb32)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const _Float16* vp = vbuf + (32 * kb32 + 16 * t + vr) * L::VP + vc;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-                        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * db));
-                        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 32 * db + 4 * L::VP));
-                        f16x4 flo = __builtin_bit_cast(f16x4, lo);
-                        f16x4 fhi = __builtin_bit_cast(f16x4, hi);
-                        f16x8 av = __builtin_shufflevector(flo, fhi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[kb32][t], o[db], 0, 0, 0);
-                    }
-                }
-        }
-
+        if (wave_active) tile(std::false_type{}, kt, i8_cur);
+        if (more) lstore((kt + 1) & 1, i8_next);
+        __syncthreads();
+    }
+    for (; kt < nkt; ++kt) {
+        const bool i8_cur = i8_next;
+        const bool more = kt + 1 < nkt;
+        i8_next = ROUTED && more && route_bit(rrow, kt + 1, a.tiles_per_bit);
+        if (more) gload(kt + 1, i8_next);
+        if (kt < w_nkt) tile(std::true_type{}, kt, i8_cur);
         if (more) lstore((kt + 1) & 1, i8_next);
         __syncthreads();
     }

@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Attention forward throughput on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole forward path over the workload's batch of
+synthetic input (for the default workload: one non-causal and one causal
+call on the same Q/K/V).  Inputs are resident in HBM before the timed
+region starts.  The value is the throughput convention of the "Nax Refactor"
+timing tables (ml-explore/mlx pull request 3271): 4*B*n_qh*qsl*ksl*hdim FLOP
+per call, halved when causal, divided by wall time.
+
+Printed: one JSON line with the metric, a roofline record of the dominant
+kernel (its per-launch time measured with HIP events on its own stream) and
+the CPU oracle's throughput on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+FP16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense fp16 MFMA
+INT8_PEAK_TOPS = 5033.2
+METRIC = "attention fwd TFLOP/s (4·B·n_qh·qsl·ksl·d, causal halved) and % MFMA peak"
+
+# The page's fused-kernel figures for the same shapes (hardware not stated on
+# the page): TFLOP/s as printed and the printed time per 64 calls.
+PAGE_ROWS = {  # (qsl, ksl, hdim, n_qh, n_kvh, causal) -> (t_fus for 64 calls, tflops)
+    (1024, 1024, 64, 32, 32, 0): (0.039, 14.263),
+    (1024, 1024, 64, 32, 32, 1): (0.022, 12.252),
+    (4096, 4096, 128, 32, 8, 1): (0.685, 12.834),
+    (512, 4096, 128, 32, 8, 1): (0.168, 6.548),
+}
+
+# default workload: dense 1024 x 1024, hdim 64, 32 heads, non-causal + causal
+BENCH_SETS = {
+    "dense_1024_d64_pair": ["dense_1024_d64", "dense_1024_d64_causal"],
+}
+for _n in W.WORKLOADS:
+    BENCH_SETS.setdefault(_n, [_n])
+
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+KERNEL_SOURCE = os.path.join(ROOT, "attention_prefill_amd", "csrc", "attn_kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dense_1024_d64_pair", choices=sorted(BENCH_SETS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp16-compare", action="store_true",
+                    help="routed workloads: also time the same inputs without a bitmask")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (reference for HBM byte counters) and exit")
+    return ap.parse_args()
+
+
+class Call:
+    """One forward call of a workload with its device inputs."""
+
+    def __init__(self, w, A, torch):
+        self.w = w
+        q, k, v = W.draw_qkv(w)
+        self.host = (q, k, v)
+        self.q, self.k, self.v = (torch.from_numpy(a).cuda() for a in (q, k, v))
+        self.out = torch.empty_like(self.q)
+        self.cu = torch.from_numpy(W.cu_seqlens_of(w.seqlens)).cuda() if w.varlen else None
+        r = W.route_for(w)
+        self.route_host = r
+        self.route = None if r is None else torch.from_numpy(r.view(np.int32)).cuda()
+        self.A = A
+        self.metric_flop, self.visited_flop = W.workload_flop(w)
+
+    def __call__(self, stream, use_route=True):
+        w = self.w
+        B = len(w.seqlens) if w.varlen else w.B
+        self.A.attn_fwd_stream(self.q, self.k, self.v, self.out, B, w.qsl, w.ksl, w.hdim, w.n_qh,
+                               w.n_kvh, w.scale, w.causal, self.cu,
+                               self.route if use_route else None, w.tiles_per_bit or 4, stream)
+
+
+def cpu_baseline(calls, budget_s=12.0):
+    """The oracle, untuned, on a bounded sample: whole query heads of each call
+    (full sequence length, the same inputs), as many as fit the time budget."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(16, os.cpu_count() or 1)
+    flop = secs = 0.0
+    samples = []
+    for c in calls:
+        w = c.w
+        q, k, v = c.host
+        G = w.n_qh // w.n_kvh
+        cu = W.cu_seqlens_of(w.seqlens) if w.varlen else None
+        spent = 0.0
+        heads = 0
+        for h in range(w.n_qh):
+            if heads and spent > budget_s / len(calls):
+                break
+            hk = h // G
+            if w.varlen:
+                qs, ks, vs = q[h:h + 1], k[hk:hk + 1], v[hk:hk + 1]
+            else:
+                qs, ks, vs = q[:, h:h + 1], k[:, hk:hk + 1], v[:, hk:hk + 1]
+            t0 = time.perf_counter()
+            oracle.attn_fwd(np.ascontiguousarray(qs), np.ascontiguousarray(ks), np.ascontiguousarray(vs),
+                            scale=w.scale, causal=w.causal, cu_seqlens=cu, route=c.route_host,
+                            tiles_per_bit=w.tiles_per_bit or 4, nthreads=threads)
+            spent += time.perf_counter() - t0
+            heads += 1
+        flop += c.metric_flop * heads / w.n_qh
+        secs += spent
+        samples.append("%s: %d of %d query heads" % (w.name, heads, w.n_qh))
+    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(samples) + ", full sequence length, same inputs; %.1f s" % secs}
+
+
+def hbm_traffic(dominant_name):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        ent = rec["kernels"].get(dominant_name)
+        if not ent:
+            return None
+        return (ent["fetch_kib"] + ent["write_kib"]) * 1024.0 * rec["copy_scale"]
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()           # default priority
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
+
+    import attention_prefill_amd as A
+    A.load()
+    names = BENCH_SETS[args.workload]
+    calls = [Call(W.WORKLOADS[n], A, torch) for n in names]
+    torch.cuda.synchronize()
+
+    def step():
+        for c in calls:
+            c(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # dominant kernel: the call with the most FLOP; HIP events on its stream
+    dom = max(range(len(calls)), key=lambda i: calls[i].visited_flop)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, c in enumerate(calls):
+            if i == dom:
+                ev[s][0].record(stream)
+            c(stream)
+            if i == dom:
+                ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    sec_per_step = (t1 - t0) / args.steps
+    metric_flop = sum(c.metric_flop for c in calls)
+    value = metric_flop / sec_per_step / 1e12
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    dc = calls[dom]
+    achieved = dc.visited_flop / (dom_ms * 1e-3) / 1e12
+    dw = dc.w
+    dom_name = "attn_fwd_kernel hd%d %s%s%s" % (dw.hdim, "causal" if dw.causal else "noncausal",
+                                                 " varlen" if dw.varlen else "",
+                                                 " routed" if dw.tiles_per_bit else "")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP16_PEAK_TFLOPS, 4),
+                "traffic": hbm_traffic(dom_name), "kernel": dom_name,
+                "flop_per_launch": dc.visited_flop, "avg_launch_ms": round(dom_ms, 5)}
+
+    # the page's figures for the same shapes, combined like the value
+    page = []
+    for c in calls:
+        w = c.w
+        key = (w.qsl, w.ksl, w.hdim, w.n_qh, w.n_kvh, int(w.causal))
+        if w.B == 1 and not w.varlen and not w.tiles_per_bit and key in PAGE_ROWS:
+            page.append(PAGE_ROWS[key][0] / 64.0)
+    vs = None
+    if len(page) == len(calls):
+        vs = round(value / (metric_flop / sum(page) / 1e12), 3)
+
+    w0 = calls[0].w
+    cfg = {"workload": args.workload, "B": len(w0.seqlens) if w0.varlen else w0.B, "qsl": w0.qsl,
+           "ksl": w0.ksl, "hdim": w0.hdim, "n_qh": w0.n_qh, "n_kvh": w0.n_kvh,
+           "causal": [c.w.causal for c in calls] if len(calls) > 1 else w0.causal,
+           "seqlens": w0.seqlens, "tiles_per_bit": w0.tiles_per_bit or None,
+           "calls_per_step": len(calls)}
+    rec = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": vs, "dtype": "fp16",
+           "data": "synthetic: i.i.d. N(0,1) Q/K/V cast to fp16 (numpy default_rng, seeded)",
+           "config": cfg, "pct_fp16_peak": round(100 * value / FP16_PEAK_TFLOPS, 2),
+           "roofline": roofline}
+    if args.fp16_compare and any(c.route is not None for c in calls):
+        for _ in range(args.warmup):
+            for c in calls:
+                c(stream, use_route=False)
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for _ in range(args.steps):
+            for c in calls:
+                c(stream, use_route=False)
+        torch.cuda.synchronize()
+        fp16_step = (time.perf_counter() - ta) / args.steps
+        rec["all_fp16_ms_per_step"] = round(fp16_step * 1e3, 5)
+        rec["routed_speedup_vs_all_fp16"] = round(fp16_step / sec_per_step, 4)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(calls)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
