@@ -138,7 +138,7 @@ def hbm_traffic(dominant_name):
         ent = rec["kernels"].get(dominant_name)
         if not ent:
             return None
-        return (ent["fetch_kib"] + ent["write_kib"]) * 1024.0 * rec["copy_scale"]
+        return ent["fetch_kib"] * 1024.0 * rec["fetch_scale"] + ent["write_kib"] * 1024.0 * rec["write_scale"]
     except (OSError, ValueError, KeyError):
         return None
 
