@@ -1,5 +1,5 @@
 // attn_api.cpp -- the C ABI declared in include/attn.h: argument validation
-// (on the host, before any device work), scratch for routed calls, dispatch
+// (on the host, before any device work), stream-ordered scratch, dispatch
 // to the kernel launchers, and error reporting.
 #include "attn.h"
 
@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <string>
 
 #include "attn_internal.h"
@@ -66,14 +67,30 @@ attn_status validate(const attn::Problem& p) {
     return ATTN_OK;
 }
 
+// Scratch comes from the device's default stream-ordered pool.  Its release
+// threshold is raised once per device so that freed blocks stay cached for
+// the next call instead of going back to the driver at every synchronise.
+void keep_pool_cached() {
+    static bool done[64] = {false};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || done[dev]) return;
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+        uint64_t keep = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    }
+    done[dev] = true;
+}
+
 attn_status run_forward(const attn::Problem& p, hipStream_t st) {
     attn_status vs = validate(p);
     if (vs != ATTN_OK) return vs;
     void* scratch = nullptr;
-    const size_t sbytes = attn::routed_scratch_bytes(p);
+    const size_t sbytes = attn::forward_scratch_bytes(p);
     if (sbytes) {
+        keep_pool_cached();
         hipError_t e = hipMallocAsync(&scratch, sbytes, st);
-        if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of routed scratch");
+        if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of forward scratch");
     }
     hipError_t e = attn::launch_forward(p, scratch, st);
     if (scratch) {

@@ -21,11 +21,12 @@ struct Problem {
     int tiles_per_bit;
 };
 
-// Device scratch the routed path needs for quantised K rows (bytes).
-size_t routed_scratch_bytes(const Problem& p);
+// Device scratch a forward call needs (bytes): quantised K rows for routed
+// calls and split-key partials when the key range is split.  0 if none.
+size_t forward_scratch_bytes(const Problem& p);
 
 // Enqueue the whole forward pass on stream.  scratch must hold
-// routed_scratch_bytes(p) bytes when p.route != nullptr (else may be null).
+// forward_scratch_bytes(p) bytes (may be null when that is 0).
 hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t stream);
 
 // Test hooks (include/attn.h).

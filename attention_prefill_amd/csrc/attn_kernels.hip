@@ -35,6 +35,7 @@
 //     1.5*2^23), int32 dot products, dequantised as dot * (s_k*c) * s_q.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <math.h>
 
 #include <type_traits>
@@ -54,8 +55,14 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BN = 64;          // keys per tile
+constexpr int TK = 64;          // keys per routing tile
 constexpr int TQ = 64;          // query rows per routing tile
+#ifndef ATTN_KEY_TILE
+#define ATTN_KEY_TILE 64
+#endif
+constexpr int BN = ATTN_KEY_TILE;   // keys per kernel tile (64 or 32)
+static_assert(BN == 64 || BN == 32, "key tile must be 64 or 32");
+constexpr int NKB = BN / 32;        // 32-key score blocks per tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23
 // dword 3 of a raw buffer descriptor (32-bit data format, no swizzle, no
@@ -174,6 +181,10 @@ struct FwdArgs {
     int tiles_per_bit, wpr;
     float c;                // |scale| * log2(e)
     int neg;                // scale < 0: queries are negated
+    int ksplit;             // key-range splits per query block (1: write out directly)
+    float* part_o;          // split partials: [ksplit, rows, HD] O / l (fp32)
+    float* part_l;          // and [ksplit, rows] log2 of the softmax denominator, base-2 units
+    long long part_rows;    // output rows (B * n_qh * qsl, or n_qh * T)
 };
 
 // Running max starts finite so that no exp2 argument is ever (-inf) - (-inf).
@@ -188,15 +199,16 @@ constexpr float TAU = 8.0f;
 // Fused forward kernel.
 // ---------------------------------------------------------------------------
 template <int HD, int NW, bool CAUSAL, bool VARLEN, bool ROUTED>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void attn_fwd_kernel(FwdArgs a) {
     using L = Lds<HD>;
     constexpr int NT = NW * 64;
-    constexpr int KCH = BN * HD / 8 / NT;              // 16-byte fp16 K chunks per thread
-    constexpr int K8CH = BN * HD / 16 / NT;            // 16-byte INT8 K chunks per thread
+    constexpr int KTOT = BN * HD / 8;                  // 16-byte fp16 K chunks per tile
+    constexpr int K8TOT = BN * HD / 16;                // 16-byte INT8 K chunks per tile
+    constexpr int KCH = (KTOT + NT - 1) / NT;          // ... per thread
+    constexpr int K8CH = (K8TOT + NT - 1) / NT;
     constexpr int VBLK = (BN / 4) * (HD / 8);          // 4-key x 8-d V blocks per tile
     constexpr int VB = (VBLK + NT - 1) / NT;           // V blocks per thread
     constexpr int NDB = HD / 32;                       // 32-row blocks of d in O^T
-    static_assert(KCH >= 1 && K8CH >= 1, "tile too small for the workgroup");
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -210,7 +222,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
 
     // ---- work decomposition -------------------------------------------------
     const int combo = blockIdx.x % a.combos;
-    const int rank = blockIdx.x / a.combos;
+    const int split = (blockIdx.x / a.combos) % a.ksplit;
+    const int rank = blockIdx.x / (a.combos * a.ksplit);
     const int hpc = a.G / HPW;
     const int hsub = combo % hpc;
     const int hk = (combo / hpc) % a.n_kvh;
@@ -259,6 +272,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
                     : CAUSAL ? min(n_kt, (min(r0 + 31, Lq - 1) + off) / BN + 1) : n_kt;
 
     const uint32_t* rrow = ROUTED ? a.route + (size_t)(m0 / TQ) * a.wpr : nullptr;
+    // route of kernel tile kt: the bit of its 64-key routing tile
+    auto tile_i8 = [&](int kt) __attribute__((always_inline)) {
+        return route_bit(rrow, (kt * BN) / TK, a.tiles_per_bit);
+    };
 
     // ---- query rows into the score B-operand layout ---------------------------
     const int qi = r0 + lq;
@@ -314,7 +331,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int n = 0; n < K8CH; ++n) {
                 const int c = tid + n * NT;     // row c / (HD/16), 16-byte column c % (HD/16)
-                kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k8rs, c * 16, soff, 0));
+                if (K8TOT % NT == 0 || c < K8TOT)
+                    kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k8rs, c * 16, soff, 0));
             }
             if (tid < BN / 4)
                 skreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(skrs, tid * 16, kt * BN * 4, 0));
@@ -323,7 +341,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int n = 0; n < KCH; ++n) {
                 const int c = tid + n * NT;     // row c / (HD/8), 16-byte column c % (HD/8)
-                kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, c * 16, soff, 0));
+                if (KTOT % NT == 0 || c < KTOT)
+                    kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, c * 16, soff, 0));
             }
         }
         const int soff = kt * BN * HD * 2;
@@ -350,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
                 const int c = tid + n * NT;
                 const int row = c / (HD / 16);
                 const int col = (c % (HD / 16)) * 16;
-                *(u32x4*)(kbuf + row * L::K8P + col) = kreg[n];
+                if (K8TOT % NT == 0 || c < K8TOT) *(u32x4*)(kbuf + row * L::K8P + col) = kreg[n];
             }
             if (tid < BN / 4) {
                 float* skc = (float*)(kbuf + BN * L::K8P);
@@ -364,7 +383,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
                 const int c = tid + n * NT;
                 const int row = c / (HD / 8);
                 const int col = (c % (HD / 8)) * 8;
-                *(u32x4*)(k16 + row * L::KP + col) = kreg[n];
+                if (KTOT % NT == 0 || c < KTOT) *(u32x4*)(k16 + row * L::KP + col) = kreg[n];
             }
         }
 #pragma unroll
@@ -404,12 +423,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const char* kbuf = smem + (kt & 1) * L::STAGE;
         const _Float16* vt = (const _Float16*)(kbuf + L::KREG);
-        float x[2][16];
+        float x[NKB][16];
         float amul;
         if (ROUTED && i8) {
             const float* skc = (const float*)(kbuf + BN * L::K8P);
 #pragma unroll
-            for (int kb32 = 0; kb32 < 2; ++kb32) {
+            for (int kb32 = 0; kb32 < NKB; ++kb32) {
                 i32x16 acc = i32x16{};
                 const int8_t* kr = (const int8_t*)kbuf + (32 * kb32 + krow) * L::K8P + 16 * g;
 #pragma unroll
@@ -435,7 +454,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         } else {
             const _Float16* k16 = (const _Float16*)kbuf;
 #pragma unroll
-            for (int kb32 = 0; kb32 < 2; ++kb32) {
+            for (int kb32 = 0; kb32 < NKB; ++kb32) {
                 f32x16 acc = f32x16{};
                 const _Float16* kr = k16 + (32 * kb32 + krow) * L::KP + 16 * g;
 #pragma unroll
@@ -454,7 +473,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
             const int lim = CAUSAL ? min(Lk - 1, qi + off) : Lk - 1;
             const int kl = kt * BN + 8 * g;
 #pragma unroll
-            for (int kb32 = 0; kb32 < 2; ++kb32)
+            for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     if (kl + 32 * kb32 + (i % 8) + 16 * (i / 8) > lim) x[kb32][i] = -INFINITY;
@@ -463,7 +482,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
         // online softmax in base 2 with a lazily moved reference max
         float mt = -INFINITY;
 #pragma unroll
-        for (int kb32 = 0; kb32 < 2; ++kb32)
+        for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mt = fmaxf(mt, x[kb32][i]);
         mt = halfwave_max(mt) * amul;
@@ -476,10 +495,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
             for (int db = 0; db < NDB; ++db) o[db] *= alpha;
         }
         const float nm = -m_run;
-        f16x8 pk[2][2];
+        f16x8 pk[NKB][2];
         float rs = 0.0f;
 #pragma unroll
-        for (int kb32 = 0; kb32 < 2; ++kb32)
+        for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -490,10 +509,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
                 }
         l_run += rs;
 
-        // O^T += V^T P^T over the four 16-key steps of the tile
+        // O^T += V^T P^T over the 16-key steps of the tile
         const _Float16* vrow = vt + lq * L::VTP + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 2 * NKB; ++kk)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const f16x8 av = *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
@@ -505,36 +524,61 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(FwdArgs a) {
     // rest (the causal diagonal and a partial last tile) go through the
     // masked variant.  Two loops keep the two variants' live ranges apart.
     const int nfull = min(nkt, min(Lk / BN, CAUSAL ? (m0 + off + 1) / BN : nkt));
+    // this workgroup's share of the key tiles when the key range is split
+    const int chunk = (nkt + a.ksplit - 1) / a.ksplit;
+    const int kt0 = min(nkt, split * chunk);
+    const int kt1 = min(nkt, kt0 + chunk);
 
-    bool i8_next = ROUTED && nkt > 0 && route_bit(rrow, 0, a.tiles_per_bit);
-    if (nkt > 0) {
-        gload(0, i8_next);
-        lstore(0, i8_next);
+    bool i8_next = ROUTED && kt0 < kt1 && tile_i8(kt0);
+    if (kt0 < kt1) {
+        gload(kt0, i8_next);
+        lstore(kt0 & 1, i8_next);
     }
     __syncthreads();
 
-    int kt = 0;
-    for (; kt < nfull; ++kt) {
+    int kt = kt0;
+    for (; kt < min(nfull, kt1); ++kt) {
         const bool i8_cur = i8_next;
-        const bool more = kt + 1 < nkt;
-        i8_next = ROUTED && more && route_bit(rrow, kt + 1, a.tiles_per_bit);
+        const bool more = kt + 1 < kt1;
+        i8_next = ROUTED && more && tile_i8(kt + 1);
         if (more) gload(kt + 1, i8_next);
         if (wave_active) tile(std::false_type{}, kt, i8_cur);
         if (more) lstore((kt + 1) & 1, i8_next);
         __syncthreads();
     }
-    for (; kt < nkt; ++kt) {
+    for (; kt < kt1; ++kt) {
         const bool i8_cur = i8_next;
-        const bool more = kt + 1 < nkt;
-        i8_next = ROUTED && more && route_bit(rrow, kt + 1, a.tiles_per_bit);
+        const bool more = kt + 1 < kt1;
+        i8_next = ROUTED && more && tile_i8(kt + 1);
         if (more) gload(kt + 1, i8_next);
         if (kt < w_nkt) tile(std::true_type{}, kt, i8_cur);
         if (more) lstore((kt + 1) & 1, i8_next);
         __syncthreads();
     }
 
-    // ---- epilogue: O / l -> fp16 ---------------------------------------------------
+    // ---- epilogue: O / l -> fp16, or a split partial --------------------------------
     const float l_tot = halfwave_sum(l_run);
+    if (a.ksplit > 1) {
+        if (wave_active && qi < Lq) {
+            // keys of this split: O / l and m + log2(l); a split with no visible key
+            // for the row contributes nothing (-inf)
+            const bool any = l_tot > 0.0f;
+            const float inv_l = any ? 1.0f / l_tot : 0.0f;
+            const size_t prow = (size_t)split * a.part_rows + qrow0 + qi;
+            float* po = a.part_o + prow * HD + 4 * g;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    f32x4 fv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) fv[e] = o[db][4 * r + e] * inv_l;
+                    *(f32x4*)(po + 32 * db + 8 * r) = fv;
+                }
+            if (g == 0) a.part_l[prow] = any ? m_run + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+        }
+        return;
+    }
     if (wave_active && qi < Lq) {
         const float inv_l = 1.0f / l_tot;
         _Float16* op = ob + (size_t)qi * HD + 4 * g;
@@ -583,6 +627,44 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const _Float16* __re
     }
 }
 
+// ---------------------------------------------------------------------------
+// Merge of split-key partials: out = sum_s w_s O_s / sum_s w_s with
+// w_s = 2^(L_s - max L), the same rescale the online softmax applies.
+// HD/8 lanes per row, 8 values per lane.
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_l,
+                                                           _Float16* __restrict__ out,
+                                                           long long rows, int ks) {
+    constexpr int LPR = HD / 8;
+    const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long row = gt / LPR;
+    const int part = (int)(gt % LPR);
+    if (row >= rows) return;
+    float mx = -INFINITY;
+    for (int sp = 0; sp < ks; ++sp) mx = fmaxf(mx, part_l[sp * rows + row]);
+    f32x4 a0 = f32x4{}, a1 = f32x4{};
+    float wsum = 0.0f;
+    for (int sp = 0; sp < ks; ++sp) {
+        const float lv = part_l[sp * rows + row];
+        if (lv == -INFINITY) continue;
+        const float wv = __builtin_amdgcn_exp2f(lv - mx);
+        const float* src = part_o + ((size_t)sp * rows + row) * HD + part * 8;
+        a0 += wv * *(const f32x4*)src;
+        a1 += wv * *(const f32x4*)(src + 4);
+        wsum += wv;
+    }
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    f16x8 hv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hv[e] = (_Float16)(a0[e] * inv);
+        hv[4 + e] = (_Float16)(a1[e] * inv);
+    }
+    *(f16x8*)(out + row * HD + part * 8) = hv;
+}
+
 // Test hook path 1: the query prologue quantiser on 32-row blocks.
 template <int HD>
 __global__ __launch_bounds__(64) void quantize_qrows_kernel(const _Float16* __restrict__ x,
@@ -611,13 +693,13 @@ __global__ __launch_bounds__(64) void quantize_qrows_kernel(const _Float16* __re
 // Test hook: the route each (query tile, key tile) takes in the forward kernel.
 __global__ void route_dump_kernel(const uint32_t* route, int qsl, int ksl, int causal,
                                   int tiles_per_bit, int wpr, uint8_t* out) {
-    const int n_kt = (ksl + BN - 1) / BN;
+    const int n_kt = (ksl + TK - 1) / TK;
     const int n_qt = (qsl + TQ - 1) / TQ;
     const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (long long)n_qt * n_kt) return;
     const int qt = (int)(idx / n_kt), kt = (int)(idx % n_kt);
     const int last_row = min(qt * TQ + TQ, qsl) - 1;
-    const bool visited = !causal || kt * BN <= last_row + (ksl - qsl);
+    const bool visited = !causal || kt * TK <= last_row + (ksl - qsl);
     uint8_t r = 2;
     if (visited) r = (route != nullptr && route_bit(route + (size_t)qt * wpr, kt, tiles_per_bit)) ? 1 : 0;
     out[idx] = r;
@@ -646,21 +728,17 @@ hipError_t dispatch_flags(const FwdArgs& a, int grid, bool causal, bool varlen, 
         return causal ? launch_fwd_t<HD, NW, true, false, true>(a, grid, st)
                       : launch_fwd_t<HD, NW, false, false, true>(a, grid, st);
     }
-    if (varlen)
-        return causal ? launch_fwd_t<HD, NW, true, true, false>(a, grid, st)
-                      : launch_fwd_t<HD, NW, false, true, false>(a, grid, st);
-    return causal ? launch_fwd_t<HD, NW, true, false, false>(a, grid, st)
-                  : launch_fwd_t<HD, NW, false, false, false>(a, grid, st);
+    if constexpr (NW == 4) {
+        if (varlen)
+            return causal ? launch_fwd_t<HD, NW, true, true, false>(a, grid, st)
+                          : launch_fwd_t<HD, NW, false, true, false>(a, grid, st);
+        return causal ? launch_fwd_t<HD, NW, true, false, false>(a, grid, st)
+                      : launch_fwd_t<HD, NW, false, false, false>(a, grid, st);
+    }
+    return hipErrorInvalidConfiguration;   // two-wave workgroups exist for routed calls only
 }
 
 }  // namespace
-
-size_t routed_scratch_bytes(const Problem& p) {
-    if (!p.route) return 0;
-    const size_t rows = (size_t)p.B * p.n_kvh * p.ksl;
-    const size_t k8 = (rows * p.hdim + 255) / 256 * 256;
-    return k8 + rows * sizeof(float);
-}
 
 hipError_t launch_quantize_rows(const void* x, int rows, int hdim, int8_t* q8, float* s,
                                 int path, hipStream_t st) {
@@ -688,7 +766,7 @@ hipError_t launch_quantize_rows(const void* x, int rows, int hdim, int8_t* q8, f
 
 hipError_t launch_route_dump(const uint32_t* route, int qsl, int ksl, bool causal,
                              int tiles_per_bit, uint8_t* out, hipStream_t st) {
-    const int n_kt = (ksl + BN - 1) / BN;
+    const int n_kt = (ksl + TK - 1) / TK;
     const int n_qt = (qsl + TQ - 1) / TQ;
     const int n_g = (n_kt + tiles_per_bit - 1) / tiles_per_bit;
     const int wpr = (n_g + 31) / 32;
@@ -699,13 +777,83 @@ hipError_t launch_route_dump(const uint32_t* route, int qsl, int ksl, bool causa
     return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
 static int largest_div(int G, int cap) {
     for (int d = cap; d > 1; d >>= 1)
         if (G % d == 0) return d;
     return 1;
 }
 
+// Launch plan of one forward call: workgroup shape, key splits, scratch layout.
+struct Plan {
+    int NW, HPW, BM, combos, n_mblk, ksplit;
+    long long grid;
+    size_t k8_off, sk_off, po_off, pl_off, bytes;   // scratch layout (bytes)
+    long long out_rows;
+};
+
+static size_t round_up(size_t x) { return (x + 255) / 256 * 256; }
+
+static Plan make_plan(const Problem& p) {
+    Plan pl{};
+    const bool varlen = p.cu_seqlens != nullptr;
+    const bool routed = p.route != nullptr;
+    const int G = p.n_qh / p.n_kvh;
+    // workgroup shape: a routed workgroup stays inside one 64-row query tile
+    pl.NW = 4;
+    pl.HPW = largest_div(G, 4);
+    if (routed && pl.HPW == 1) pl.NW = 2;
+    pl.BM = (pl.NW / pl.HPW) * 32;
+    pl.combos = (varlen ? 1 : p.B) * p.n_kvh * (G / pl.HPW);
+    pl.n_mblk = varlen ? (p.qsl + pl.BM - 1) / pl.BM + p.B : (p.qsl + pl.BM - 1) / pl.BM;
+    // Split the key range when the grid leaves SIMDs without a wavefront (the
+    // partials and their merge cost more than they return otherwise): up to
+    // two wavefronts per SIMD, keeping at least eight tiles per split.
+    const long long waves = (long long)pl.combos * pl.n_mblk * pl.NW;
+    const long long simds = 4LL * cu_count();
+    const int n_kt = (p.ksl + BN - 1) / BN;
+    int ks = 1;
+    if (waves < simds)
+        while (ks < 8 && waves * ks < 2 * simds && n_kt >= 16 * ks) ks *= 2;
+    const char* force = getenv("ATTN_KSPLIT");
+    if (force && force[0] >= '1' && force[0] <= '8' && force[1] == 0) ks = force[0] - '0';
+    pl.ksplit = ks;
+    pl.grid = (long long)pl.combos * pl.ksplit * pl.n_mblk;
+    pl.out_rows = varlen ? (long long)p.n_qh * p.qsl : (long long)p.B * p.n_qh * p.qsl;
+    size_t off = 0;
+    if (routed) {
+        const size_t krows = (size_t)p.B * p.n_kvh * p.ksl;
+        pl.k8_off = off;
+        off += round_up(krows * p.hdim);
+        pl.sk_off = off;
+        off += round_up(krows * sizeof(float));
+    }
+    if (pl.ksplit > 1) {
+        pl.po_off = off;
+        off += round_up((size_t)pl.ksplit * pl.out_rows * p.hdim * sizeof(float));
+        pl.pl_off = off;
+        off += round_up((size_t)pl.ksplit * pl.out_rows * sizeof(float));
+    }
+    pl.bytes = off;
+    return pl;
+}
+
+size_t forward_scratch_bytes(const Problem& p) { return make_plan(p).bytes; }
+
 hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
+    const Plan pl = make_plan(p);
     FwdArgs a;
     a.q = (const _Float16*)p.q;
     a.k = (const _Float16*)p.k;
@@ -724,42 +872,49 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
     a.tiles_per_bit = p.route ? p.tiles_per_bit : 1;
     a.k8 = nullptr;
     a.sk = nullptr;
+    a.HPW = pl.HPW;
+    a.combos = pl.combos;
+    a.n_mblk = pl.n_mblk;
+    a.ksplit = pl.ksplit;
+    a.part_rows = pl.out_rows;
+    a.part_o = pl.ksplit > 1 ? (float*)((char*)scratch + pl.po_off) : nullptr;
+    a.part_l = pl.ksplit > 1 ? (float*)((char*)scratch + pl.pl_off) : nullptr;
     const bool varlen = p.cu_seqlens != nullptr;
     const bool routed = p.route != nullptr;
 
-    // workgroup shape: a routed workgroup stays inside one 64-row query tile
-    int NW = 4;
-    int HPW = largest_div(a.G, 4);
-    if (routed && HPW == 1) NW = 2;
-    a.HPW = HPW;
-    const int BM = (NW / HPW) * 32;
-    const int hpc = a.G / HPW;
-    a.combos = (varlen ? 1 : p.B) * p.n_kvh * hpc;
-    a.n_mblk = varlen ? (p.qsl + BM - 1) / BM + p.B : (p.qsl + BM - 1) / BM;
-
     if (routed) {
-        const int n_kt = (p.ksl + BN - 1) / BN;
+        const int n_kt = (p.ksl + TK - 1) / TK;
         const int n_g = (n_kt + p.tiles_per_bit - 1) / p.tiles_per_bit;
         a.wpr = (n_g + 31) / 32;
-        const size_t rows = (size_t)p.B * p.n_kvh * p.ksl;
-        const size_t k8bytes = (rows * p.hdim + 255) / 256 * 256;
-        a.k8 = (const int8_t*)scratch;
-        a.sk = (const float*)((char*)scratch + k8bytes);
-        hipError_t e = launch_quantize_rows(p.k, (int)rows, p.hdim, (int8_t*)a.k8, (float*)a.sk, 0, st);
+        const size_t krows = (size_t)p.B * p.n_kvh * p.ksl;
+        a.k8 = (const int8_t*)((char*)scratch + pl.k8_off);
+        a.sk = (const float*)((char*)scratch + pl.sk_off);
+        hipError_t e = launch_quantize_rows(p.k, (int)krows, p.hdim, (int8_t*)a.k8, (float*)a.sk, 0, st);
         if (e != hipSuccess) return e;
     } else {
         a.wpr = 0;
     }
 
-    const long long grid_ll = (long long)a.combos * a.n_mblk;
-    if (grid_ll <= 0) return hipSuccess;
-    if (grid_ll > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const int grid = (int)grid_ll;
+    if (pl.grid <= 0) return hipSuccess;
+    if (pl.grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int grid = (int)pl.grid;
+    hipError_t e;
     if (p.hdim == 64)
-        return NW == 4 ? dispatch_flags<64, 4>(a, grid, p.causal, varlen, routed, st)
+        e = pl.NW == 4 ? dispatch_flags<64, 4>(a, grid, p.causal, varlen, routed, st)
                        : dispatch_flags<64, 2>(a, grid, p.causal, varlen, routed, st);
-    return NW == 4 ? dispatch_flags<128, 4>(a, grid, p.causal, varlen, routed, st)
-                   : dispatch_flags<128, 2>(a, grid, p.causal, varlen, routed, st);
+    else
+        e = pl.NW == 4 ? dispatch_flags<128, 4>(a, grid, p.causal, varlen, routed, st)
+                       : dispatch_flags<128, 2>(a, grid, p.causal, varlen, routed, st);
+    if (e != hipSuccess || pl.ksplit == 1) return e;
+    const long long threads = pl.out_rows * (p.hdim / 8);
+    const int mgrid = (int)((threads + 255) / 256);
+    if (p.hdim == 64)
+        hipLaunchKernelGGL(merge_splits_kernel<64>, dim3(mgrid), dim3(256), 0, st, a.part_o, a.part_l,
+                           a.out, pl.out_rows, pl.ksplit);
+    else
+        hipLaunchKernelGGL(merge_splits_kernel<128>, dim3(mgrid), dim3(256), 0, st, a.part_o, a.part_l,
+                           a.out, pl.out_rows, pl.ksplit);
+    return hipGetLastError();
 }
 
 }  // namespace attn

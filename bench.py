@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--workload", default="dense_1024_d64_pair", choices=sorted(BENCH_SETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fp16-compare", action="store_true",
-                    help="routed workloads: also time the same inputs without a bitmask")
+                    help="routed workloads: also time the same inputs with an all-FP16 (zero) "
+                         "bitmask and with no bitmask")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (reference for HBM byte counters) and exit")
     return ap.parse_args()
@@ -81,13 +82,16 @@ class Call:
         self.route = None if r is None else torch.from_numpy(r.view(np.int32)).cuda()
         self.A = A
         self.metric_flop, self.visited_flop = W.workload_flop(w)
+        self.zero_route = None if r is None else torch.zeros_like(self.route)
 
-    def __call__(self, stream, use_route=True):
+    def __call__(self, stream, route="drawn"):
+        """route: "drawn" (the workload's bitmask), "zero" (same kernel, every
+        tile FP16) or "none" (no bitmask: the dense kernel)."""
         w = self.w
         B = len(w.seqlens) if w.varlen else w.B
+        rt = {"drawn": self.route, "zero": self.zero_route, "none": None}[route]
         self.A.attn_fwd_stream(self.q, self.k, self.v, self.out, B, w.qsl, w.ksl, w.hdim, w.n_qh,
-                               w.n_kvh, w.scale, w.causal, self.cu,
-                               self.route if use_route else None, w.tiles_per_bit or 4, stream)
+                               w.n_kvh, w.scale, w.causal, self.cu, rt, w.tiles_per_bit or 4, stream)
 
 
 def cpu_baseline(calls, budget_s=12.0):
@@ -237,18 +241,25 @@ def main():
            "config": cfg, "pct_fp16_peak": round(100 * value / FP16_PEAK_TFLOPS, 2),
            "roofline": roofline}
     if args.fp16_compare and any(c.route is not None for c in calls):
-        for _ in range(args.warmup):
-            for c in calls:
-                c(stream, use_route=False)
-        torch.cuda.synchronize()
-        ta = time.perf_counter()
-        for _ in range(args.steps):
-            for c in calls:
-                c(stream, use_route=False)
-        torch.cuda.synchronize()
-        fp16_step = (time.perf_counter() - ta) / args.steps
-        rec["all_fp16_ms_per_step"] = round(fp16_step * 1e3, 5)
-        rec["routed_speedup_vs_all_fp16"] = round(fp16_step / sec_per_step, 4)
+        # the all-FP16 run of the same inputs: the same kernel with a zero
+        # bitmask, and for context the dense kernel with no bitmask at all
+        def time_route(route):
+            for _ in range(args.warmup):
+                for c in calls:
+                    c(stream, route)
+            torch.cuda.synchronize()
+            ta = time.perf_counter()
+            for _ in range(args.steps):
+                for c in calls:
+                    c(stream, route)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - ta) / args.steps
+        zero_step = time_route("zero")
+        dense_step = time_route("none")
+        rec["all_fp16_ms_per_step"] = round(zero_step * 1e3, 5)
+        rec["routed_speedup_vs_all_fp16"] = round(zero_step / sec_per_step, 4)
+        rec["dense_no_bitmask_ms_per_step"] = round(dense_step * 1e3, 5)
+        rec["routed_speedup_vs_dense"] = round(dense_step / sec_per_step, 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(calls)
     print(json.dumps(rec), flush=True)
