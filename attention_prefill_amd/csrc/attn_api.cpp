@@ -50,8 +50,6 @@ attn_status validate(const attn::Problem& p) {
         return fail(ATTN_ERR_SHAPE, "packed input needs qsl == ksl == total tokens (got %d, %d)", p.qsl, p.ksl);
     if (p.hdim != 64 && p.hdim != 128)
         return fail(ATTN_ERR_UNSUPPORTED, "hdim must be 64 or 128 (got %d)", p.hdim);
-    if (p.route && p.cu_seqlens)
-        return fail(ATTN_ERR_UNSUPPORTED, "a routing bitmask with packed (cu_seqlens) input is not supported");
     if (!std::isfinite(p.scale) || p.scale == 0.0f)
         return fail(ATTN_ERR_ARG, "scale must be finite and non-zero");
     if (p.route && p.tiles_per_bit < 1)

@@ -230,6 +230,7 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
     const int h = hk * a.G + hsub * HPW + (w % HPW);
 
     int mb, Lq, Lk;
+    int rrow0 = 0;                  // first routing-bitmask row of this sequence
     size_t qrow0, krow0;            // row index of row 0 of (sequence, head) in q / k
     if constexpr (VARLEN) {
         int t = rank, s = -1;
@@ -246,6 +247,10 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
         Lq = Lk = a.cu[s + 1] - start;
         qrow0 = (size_t)h * T + start;
         krow0 = (size_t)hk * T + start;
+        if constexpr (ROUTED) {
+            // sequences stack their own query-tile rows in order
+            for (int ss = 0; ss < s; ++ss) rrow0 += (a.cu[ss + 1] - a.cu[ss] + TQ - 1) / TQ;
+        }
     } else {
         const int b = combo / (hpc * a.n_kvh);
         mb = CAUSAL ? (a.n_mblk - 1 - rank) : rank;
@@ -271,7 +276,7 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
     const int w_nkt = !wave_active ? 0
                     : CAUSAL ? min(n_kt, (min(r0 + 31, Lq - 1) + off) / BN + 1) : n_kt;
 
-    const uint32_t* rrow = ROUTED ? a.route + (size_t)(m0 / TQ) * a.wpr : nullptr;
+    const uint32_t* rrow = ROUTED ? a.route + (size_t)(rrow0 + m0 / TQ) * a.wpr : nullptr;
     // route of kernel tile kt: the bit of its 64-key routing tile
     auto tile_i8 = [&](int kt) __attribute__((always_inline)) {
         return route_bit(rrow, (kt * BN) / TK, a.tiles_per_bit);
@@ -724,7 +729,9 @@ template <int HD, int NW>
 hipError_t dispatch_flags(const FwdArgs& a, int grid, bool causal, bool varlen, bool routed,
                           hipStream_t st) {
     if (routed) {
-        // routed packed batches are rejected by the ABI
+        if (varlen)
+            return causal ? launch_fwd_t<HD, NW, true, true, true>(a, grid, st)
+                          : launch_fwd_t<HD, NW, false, true, true>(a, grid, st);
         return causal ? launch_fwd_t<HD, NW, true, false, true>(a, grid, st)
                       : launch_fwd_t<HD, NW, false, false, true>(a, grid, st);
     }
@@ -834,7 +841,7 @@ static Plan make_plan(const Problem& p) {
     pl.out_rows = varlen ? (long long)p.n_qh * p.qsl : (long long)p.B * p.n_qh * p.qsl;
     size_t off = 0;
     if (routed) {
-        const size_t krows = (size_t)p.B * p.n_kvh * p.ksl;
+        const size_t krows = varlen ? (size_t)p.n_kvh * p.ksl : (size_t)p.B * p.n_kvh * p.ksl;
         pl.k8_off = off;
         off += round_up(krows * p.hdim);
         pl.sk_off = off;
@@ -886,7 +893,7 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
         const int n_kt = (p.ksl + TK - 1) / TK;
         const int n_g = (n_kt + p.tiles_per_bit - 1) / p.tiles_per_bit;
         a.wpr = (n_g + 31) / 32;
-        const size_t krows = (size_t)p.B * p.n_kvh * p.ksl;
+        const size_t krows = varlen ? (size_t)p.n_kvh * p.ksl : (size_t)p.B * p.n_kvh * p.ksl;
         a.k8 = (const int8_t*)((char*)scratch + pl.k8_off);
         a.sk = (const float*)((char*)scratch + pl.sk_off);
         hipError_t e = launch_quantize_rows(p.k, (int)krows, p.hdim, (int8_t*)a.k8, (float*)a.sk, 0, st);

@@ -33,12 +33,20 @@
  *   (route_bitmask[qt * wpr + g / 32] >> (g % 32)) & 1; 1 = INT8, 0 = FP16.
  *   Tile indices count from row 0 of q and row 0 of k.  Bits of groups that
  *   the causal mask leaves empty for a query tile are ignored.
+ *   Packed input: each sequence s has its own rows, one per 64-row query tile
+ *   of that sequence (counted from its start), stacked in sequence order, so
+ *   the row of (s, qt) is qt + sum over s' < s of ceil(L_s'/64); wpr is
+ *   computed with ksl = T, and bits of groups past the sequence's own key
+ *   tiles are ignored.
  * out is fully overwritten.  Nothing the caller passes is retained.
  *
  * Calls are asynchronous: they validate the arguments on the host, enqueue
- * work on the given stream and return.  A routed call uses stream-ordered
- * device scratch (hipMallocAsync / hipFreeAsync on the same stream) for the
- * quantised K rows.  Errors are reported by the return code; a
+ * work on the given stream and return.  Routed calls (quantised K rows) and
+ * calls whose grid is split along the keys (fp32 partial results) use
+ * stream-ordered device scratch from the device's default memory pool
+ * (hipMallocAsync / hipFreeAsync on the same stream; the pool's release
+ * threshold is raised once so blocks stay cached).  Errors are reported by
+ * the return code; a
  * thread-local message is available from attn_last_error().  Argument
  * errors are detected before any device work is enqueued.
  */
@@ -56,7 +64,7 @@ typedef enum {
     ATTN_ERR_NULL = 1,         /* q, k, v or out is NULL */
     ATTN_ERR_SHAPE = 2,        /* a size <= 0, n_qh % n_kvh != 0, causal with
                                   qsl > ksl, or packed with qsl != ksl */
-    ATTN_ERR_UNSUPPORTED = 3,  /* hdim not 64 or 128; bitmask with cu_seqlens */
+    ATTN_ERR_UNSUPPORTED = 3,  /* hdim not 64 or 128 */
     ATTN_ERR_ARG = 4,          /* scale not finite or zero; tiles_per_bit < 1
                                   with a bitmask; pointer not 16-byte aligned */
     ATTN_ERR_HIP = 5           /* the HIP runtime reported an error */

@@ -43,6 +43,11 @@
  *    heads and batch elements; rows of wpr = ceil(n_groups/32) uint32 words,
  *    bit g of row qt is (w[qt*wpr + g/32] >> (g%32)) & 1; 1 = INT8.
  *    Tile indices count from row 0 of Q and row 0 of K.
+ *  - Packed batches with a bitmask: every sequence s has its own rows, one
+ *    per query tile of that sequence (tiles counted from its start), stacked
+ *    in sequence order; row r0(s) = sum over s' < s of ceil(L_s'/tile_q).
+ *    All rows have wpr words for the packed length T; bits of groups past a
+ *    sequence's own key tiles are never read.
  *  - Output is the exact fp64 result; a fp16 round-to-nearest-even encoder
  *    is provided for exact special cases.
  *
@@ -185,6 +190,19 @@ static size_t kv_base(const problem* p, int s, int hk, int* Lk)
     return (((size_t)s * p->n_kvh + hk) * p->ksl) * p->d;
 }
 
+/* First bitmask row of sequence s: 0 for dense input (rows are shared by the
+ * batch), else the query tiles of the sequences before it. */
+static int route_row0(const problem* p, int s)
+{
+    if (!p->cu) return 0;
+    int r = 0;
+    for (int t = 0; t < s; ++t) {
+        int L = p->cu[t + 1] - p->cu[t];
+        r += (L + p->tile_q - 1) / p->tile_q;
+    }
+    return r;
+}
+
 static int visible(const problem* p, int i, int j, int Lq, int Lk)
 {
     return !p->causal || j <= i + (Lk - Lq);
@@ -208,9 +226,10 @@ static void free_qrows(qrows r) { free(r.q8); free(r.s); }
 
 /* Scores of query row i against all Lk keys; masked cells get -inf. */
 static void score_row(const problem* p, const uint16_t* qrow, const uint16_t* kb,
-                      const qrows* qq, const qrows* kq, int i, int Lq, int Lk, double* S)
+                      const qrows* qq, const qrows* kq, int i, int Lq, int Lk, int rrow0,
+                      double* S)
 {
-    int qt = i / p->tile_q;
+    int qt = rrow0 + i / p->tile_q;
     for (int j = 0; j < Lk; ++j) {
         if (!visible(p, i, j, Lq, Lk)) { S[j] = -INFINITY; continue; }
         const uint16_t* krow = kb + (size_t)j * p->d;
@@ -263,7 +282,6 @@ static int check_problem(const problem* p)
     if (p->cu) {
         if (p->qsl != p->ksl || p->cu[0] != 0 || p->cu[p->B] != p->qsl) return ORACLE_ERR_ARG;
         for (int s = 0; s < p->B; ++s) if (p->cu[s + 1] < p->cu[s]) return ORACLE_ERR_ARG;
-        if (p->route) return ORACLE_ERR_ARG;   /* routed packs are not defined here */
     }
     if (p->route && (p->tiles_per_bit < 1 || p->tile_q < 1 || p->tile_k < 1)) return ORACLE_ERR_ARG;
     return 0;
@@ -307,6 +325,7 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, dou
 #endif
     int G = n_qh / n_kvh;
     for (int s = 0; s < B; ++s) {
+        const int rrow0 = route_row0(&p, s);
         for (int hk = 0; hk < n_kvh; ++hk) {
             int Lk;
             size_t kb = kv_base(&p, s, hk, &Lk);
@@ -323,7 +342,8 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, dou
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
 #endif
                 for (int i = 0; i < Lq; ++i)
-                    score_row(&p, q + qb + (size_t)i * d, k + kb, &qq, &kq, i, Lq, Lk, S + (size_t)i * Lk);
+                    score_row(&p, q + qb + (size_t)i * d, k + kb, &qq, &kq, i, Lq, Lk, rrow0,
+                              S + (size_t)i * Lk);
 #ifdef _OPENMP
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
 #endif
@@ -389,7 +409,7 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #endif
             err = ORACLE_ERR_NOMEM;
         } else {
-            score_row(&p, q + qb + (size_t)i * d, k + kb, &qq, &kq, i, Lq, Lk, S);
+            score_row(&p, q + qb + (size_t)i * d, k + kb, &qq, &kq, i, Lq, Lk, route_row0(&p, s), S);
             softmax_pv_row(&p, S, Lk, v + kb, out + (size_t)r * d);
             free(S);
         }

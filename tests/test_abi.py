@@ -52,7 +52,7 @@ def call(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, qsl=64, ksl=64, hdim=64, n_qh=4,
     (dict(n_kvh=0), SHAPE), (dict(n_qh=6, n_kvh=4), SHAPE),
     (dict(causal=1, qsl=65, ksl=64), SHAPE),
     (dict(cu=FAKE, qsl=64, ksl=63), SHAPE),
-    (dict(hdim=96), UNSUP), (dict(hdim=256), UNSUP), (dict(cu=FAKE, route=FAKE), UNSUP),
+    (dict(hdim=96), UNSUP), (dict(hdim=256), UNSUP),
     (dict(scale=float("nan")), ARG), (dict(scale=float("inf")), ARG), (dict(scale=0.0), ARG),
     (dict(route=FAKE, tpb=0), ARG),
     (dict(q=FAKE + 8), ARG), (dict(out=FAKE + 2), ARG), (dict(route=FAKE + 2), ARG),

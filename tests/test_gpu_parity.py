@@ -123,6 +123,39 @@ def test_routed_ragged(A, orc, d, heads, causal, tpb):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("heads", [(2, 2), (8, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("tpb", [1, 3, 4])
+def test_routed_varlen_ragged(A, orc, d, heads, causal, tpb):
+    """Packed batch with a bitmask: every sequence reads its own stacked rows."""
+    rng = np.random.default_rng(500 + d + 7 * heads[1] + causal + 13 * tpb)
+    lens = [1, 63, 64, 65, 200, 0, 130, 7]
+    cu = W.cu_seqlens_of(lens)
+    T = int(cu[-1])
+    n_rows = sum(-(-L // 64) for L in lens)
+    n_g = W.n_route_groups(T, tpb)
+    route = W.pack_bits(rng.random((n_rows, n_g)) < 0.5)
+    say("routed varlen d=%d heads=%s causal=%d tpb=%d" % (d, heads, causal, tpb))
+    q, k, v = rand16(rng, (heads[0], T, d)), rand16(rng, (heads[1], T, d)), rand16(rng, (heads[1], T, d))
+    got = gpu_attn(A, q, k, v, 0.1, causal, cu=cu, route=route, tpb=tpb)
+    ref = orc.attn_fwd(q, k, v, scale=0.1, causal=causal, cu_seqlens=cu, route=route, tiles_per_bit=tpb)
+    check(got, ref)
+
+
+def test_gpu_routed_varlen_zero_mask_is_dense(A):
+    rng = np.random.default_rng(510)
+    lens = [100, 1, 250, 64]
+    cu = W.cu_seqlens_of(lens)
+    T = int(cu[-1])
+    q, k, v = rand16(rng, (8, T, 128)), rand16(rng, (2, T, 128)), rand16(rng, (2, T, 128))
+    zeros = W.pack_bits(np.zeros((sum(-(-L // 64) for L in lens), W.n_route_groups(T, 4)), dtype=bool))
+    for causal in (False, True):
+        a = gpu_attn(A, q, k, v, 0.1, causal, cu=cu, route=zeros, tpb=4)
+        b = gpu_attn(A, q, k, v, 0.1, causal, cu=cu)
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_routed_all_int8(A, orc, d):
     rng = np.random.default_rng(40 + d)
     qsl = ksl = 300

@@ -83,11 +83,16 @@ def np_attention(q, k, v, scale, causal, cu=None, route=None, tpb=1, tile_q=64, 
     if cu is not None:
         out = np.zeros(q.shape, dtype=np.float64)
         G = q.shape[0] // k.shape[0]
+        r0 = 0
         for s in range(len(cu) - 1):
             a, b = cu[s], cu[s + 1]
+            n_qt = -(-(b - a) // tile_q)
+            rows = None if route is None else route[r0:r0 + n_qt]
+            r0 += n_qt
             for h in range(q.shape[0]):
                 if b > a:
-                    out[h, a:b] = np_attention_one(q[h, a:b], k[h // G, a:b], v[h // G, a:b], scale, causal)
+                    out[h, a:b] = np_attention_one(q[h, a:b], k[h // G, a:b], v[h // G, a:b], scale, causal,
+                                                   rows, tpb, tile_q, tile_k)
         return out
     B, Hq = q.shape[:2]
     G = Hq // k.shape[1]
@@ -189,6 +194,48 @@ def test_routed_vs_bruteforce(orc, tile, tpb, causal):
                            tile_q=tq, tile_k=tk)
         ref = np_attention(q, k, v, 0.125, causal, route=route, tpb=tpb, tile_q=tq, tile_k=tk)
         assert np.max(np.abs(got - ref)) <= 1e-12, (qsl, ksl)
+
+
+@pytest.mark.parametrize("tile", [(2, 2), (4, 4), (64, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_routed_varlen_vs_bruteforce(orc, tile, causal):
+    """Packed batch with a bitmask: each sequence reads its own stacked rows."""
+    tq, tk = tile
+    rng = np.random.default_rng(950 + tq + causal)
+    lens = [5, 0, 17, 1, 40]
+    cu = workloads.cu_seqlens_of(lens)
+    T = int(cu[-1])
+    tpb = 2
+    q, k, v = rand16(rng, (4, T, 64)), rand16(rng, (2, T, 64)), rand16(rng, (2, T, 64))
+    n_rows = sum(-(-L // tq) for L in lens)
+    n_g_T = -(-(-(-T // tk)) // tpb)
+    route = workloads.pack_bits(rng.random((n_rows, n_g_T)) < 0.5)
+    got = orc.attn_fwd(q, k, v, scale=0.125, causal=causal, cu_seqlens=cu, route=route, tiles_per_bit=tpb,
+                       tile_q=tq, tile_k=tk)
+    ref = np_attention(q, k, v, 0.125, causal, cu=cu, route=route, tpb=tpb, tile_q=tq, tile_k=tk)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_routed_varlen_is_per_sequence(orc):
+    rng = np.random.default_rng(960)
+    lens = [70, 1, 150]
+    cu = workloads.cu_seqlens_of(lens)
+    T = int(cu[-1])
+    q, k, v = rand16(rng, (4, T, 64)), rand16(rng, (2, T, 64)), rand16(rng, (2, T, 64))
+    n_qts = [-(-L // 64) for L in lens]
+    n_g_T = -(-(-(-T // 64)) // 1)
+    bits = rng.random((sum(n_qts), n_g_T)) < 0.5
+    route = workloads.pack_bits(bits)
+    packed = orc.attn_fwd(q, k, v, scale=0.125, causal=True, cu_seqlens=cu, route=route, tiles_per_bit=1)
+    r0 = 0
+    for s, L in enumerate(lens):
+        a, b = cu[s], cu[s + 1]
+        own = workloads.pack_bits(bits[r0:r0 + n_qts[s], :-(-L // 64)])
+        r0 += n_qts[s]
+        one = orc.attn_fwd(np.ascontiguousarray(q[None, :, a:b]), np.ascontiguousarray(k[None, :, a:b]),
+                           np.ascontiguousarray(v[None, :, a:b]), scale=0.125, causal=True, route=own,
+                           tiles_per_bit=1)
+        assert np.array_equal(packed[:, a:b], one[0])
 
 
 def test_all_ones_is_uniform_int8(orc):
