@@ -7,15 +7,20 @@
 // an INT8 QK^T score computation, and both routes update one online-softmax
 // state (running max m, running sum l, fp32 output accumulator).
 //
-// Kernel structure (one workgroup = NW wavefronts of 64 lanes):
+// Kernel structure (one workgroup = KS key groups of NW wavefronts of 64 lanes):
 //   * work decomposition: a workgroup owns HPW query heads of one kv head
 //     and BM = 32*NW/HPW query rows; every wavefront owns 32 rows of one
-//     head.  Grid order is heavy-first for causal masks and keeps the
-//     workgroups of one kv head on one XCD (index mod 8) when the number of
-//     head groups is a multiple of 8.
-//   * tile loader: 64-key K and V tiles go global -> registers -> LDS with
-//     two LDS stages, so the loads of tile t+1 are in flight while tile t is
-//     computed; one barrier per tile.
+//     head.  With KS = 2 a second group of NW wavefronts owns the same rows
+//     and takes every other key tile; the two online-softmax states merge
+//     through LDS at the end (small grids get two wavefronts per SIMD this
+//     way without a second pass).  Grid order is heavy-first for causal
+//     masks and keeps the workgroups of one kv head on one XCD (index mod 8)
+//     when the number of head groups is a multiple of 8.
+//   * tile loader: 64-key K and V tiles go global -> registers -> LDS
+//     through buffer descriptors (reads past the sequence end return zeros),
+//     with two LDS stages and one barrier per tile.  The hdim-64 FP16 kernel
+//     keeps two register sets so that the loads of tile t+2 are in flight
+//     while tile t is computed; the others load tile t+1.
 //   * score MFMA: the transposed score tile S^T = K Q^T is computed with
 //     v_mfma_f32_32x32x16_f16 (FP16 route) or v_mfma_i32_32x32x32_i8 (INT8
 //     route).  In the 32x32 accumulator layout a lane then owns one query
@@ -24,10 +29,12 @@
 //     bits 2 and 3 of the row index swapped; this makes the score layout
 //     coincide with the B-operand layout of the P.V MFMA, so P never leaves
 //     registers.
-//   * P.V MFMA: O^T += V^T P^T with v_mfma_f32_32x32x16_f16, V^T fragments
-//     read from the natural [key][d] LDS layout by ds_read_b64_tr_b16.
+//   * P.V MFMA: O^T += V^T P^T with v_mfma_f32_32x32x16_f16.  V is stored
+//     transposed in LDS ([d][key], transposed in registers by the loader),
+//     so each V^T fragment (8 keys of one d) is one 16-byte read.
 //   * online softmax in base 2 with the scale folded into one FMA per
-//     score; O is rescaled only when some row max of the wavefront moved.
+//     score; O is rescaled only when some row max of the wavefront moved by
+//     more than a threshold.
 //   * INT8 route: K rows are quantised once per call by a separate pass
 //     (quantize_rows_kernel); the query rows of a wavefront are quantised in
 //     its prologue.  Per-token symmetric codes: s = fl32(amax/127),
@@ -198,10 +205,11 @@ constexpr float TAU = 8.0f;
 // ---------------------------------------------------------------------------
 // Fused forward kernel.
 // ---------------------------------------------------------------------------
-template <int HD, int NW, bool CAUSAL, bool VARLEN, bool ROUTED>
-__global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void attn_fwd_kernel(FwdArgs a) {
+template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED>
+__global__ __launch_bounds__(NW * KS * 64, (NW == 2 || KS > 1) ? 1 : (BN == 32 ? 3 : 2))
+void attn_fwd_kernel(FwdArgs a) {
     using L = Lds<HD>;
-    constexpr int NT = NW * 64;
+    constexpr int NT = NW * 64;                        // threads of one key group
     constexpr int KTOT = BN * HD / 8;                  // 16-byte fp16 K chunks per tile
     constexpr int K8TOT = BN * HD / 16;                // 16-byte INT8 K chunks per tile
     constexpr int KCH = (KTOT + NT - 1) / NT;          // ... per thread
@@ -209,11 +217,22 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
     constexpr int VBLK = (BN / 4) * (HD / 8);          // 4-key x 8-d V blocks per tile
     constexpr int VB = (VBLK + NT - 1) / NT;           // V blocks per thread
     constexpr int NDB = HD / 32;                       // 32-row blocks of d in O^T
+    // Tiles in flight ahead of the one computed.  Two need a second staging
+    // set, which only the hdim-64 FP16 kernel has registers for.
+    constexpr int PF = (HD == 64 && !ROUTED && NW == 4 && BN == 64) ? 2 : 1;
+    // Request all of a tile's K and V fragments before its first MFMA (the
+    // hdim-64 kernel has the registers for them).
+    constexpr bool EARLY = (HD == 64);
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    // KS key groups of NW wavefronts: every group owns the same query rows and
+    // takes every KS-th key tile; their softmax states merge at the end.
+    // (wave-uniform values go through readfirstlane so that the compiler keeps
+    // them, and the buffer offsets derived from them, in scalar registers)
+    const int kgp = __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT);
+    const int tid = (int)threadIdx.x % NT;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63;
     const int g = l >> 5;
     const int lq = l & 31;
@@ -293,22 +312,10 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
             qf[2 * kb2] = *(const f16x8*)(qp + 32 * kb2);
             qf[2 * kb2 + 1] = *(const f16x8*)(qp + 32 * kb2 + 8);
         }
-        if (a.neg) {
-#pragma unroll
-            for (int t = 0; t < HD / 16; ++t) qf[t] = -qf[t];
-        }
-        // Settle the query loads here: otherwise the wait-count analysis at the
-        // loop header cannot tell them from the tile prefetches and makes every
-        // score MFMA wait for the next tile's loads.
-        __builtin_amdgcn_s_waitcnt(0);
     }
-    i32x4 q8[ROUTED ? HD / 32 : 1];
+
+    i32x4 q8[ROUTED ? HD / 32 : 1];     // INT8 query codes (routed), set after the prologue wait
     float sq_mul = 1.0f;
-    if constexpr (ROUTED) {
-        float sq;
-        quantize_q_regs<HD>(qf, q8, sq);
-        sq_mul = sq > 0.0f ? sq : 1.0f;   // a zero row has all-zero INT8 scores
-    }
 
     // ---- tile loader ------------------------------------------------------------
     // K: 16-byte chunks of rows.  V: per thread a block of 4 keys x 8 d, read as
@@ -326,11 +333,72 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
         k8rs = __builtin_amdgcn_make_buffer_rsrc((void*)k8b, (short)0, Lk * HD, BUF_DWORD3);
         skrs = __builtin_amdgcn_make_buffer_rsrc((void*)skb, (short)0, Lk * 4, BUF_DWORD3);
     }
-    u32x4 kreg[KCH];
-    u32x4 vreg[VB][4];
-    u32x4 skreg;
+    // Staging registers of one tile between its global loads and its LDS
+    // store.  With PF = 2 two sets alternate, so the loads of tile t+2 are
+    // issued while tile t is computed and have two tiles' time to land.
+    struct Staging {
+        u32x4 kreg[KCH];
+        u32x4 vreg[VB][4];
+        u32x4 skreg;
+    };
+    // The two-set pipeline waits for the older set with a load count, so every
+    // lane issues the same number of loads: the first half of the waves loads
+    // the V tile (one 4-key x 8-d block per thread), the second half the K tile
+    // (four 16-byte chunks per thread), four loads each, unconditionally
+    // (loads past the sequence end return zeros and are never used).
+    struct Staging2 {
+        u32x4 r[4];
+    };
+    using Set = typename std::conditional<PF == 2, Staging2, Staging>::type;
+    Set set0, set1;
+    const bool v_half = w < NW / 2;
+    const int th = tid % (NT / 2);
 
-    auto gload = [&](int kt, bool i8) __attribute__((always_inline)) {
+    // Branch-free loads (descriptor picked per wave, offsets per lane) so the
+    // wait-count analysis sees one straight path.
+    static_assert(PF == 1 || ((BN / 4) * (HD / 8) == NT / 2 && BN * HD / 8 == 4 * (NT / 2)),
+                  "balanced loader shape");
+    const __amdgpu_buffer_rsrc_t rs2 = v_half ? vrs : krs;
+    int voff2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        voff2[i] = v_half ? ((4 * (th % (BN / 4)) + i) * HD + 8 * (th / (BN / 4))) * 2
+                          : (th + i * (NT / 2)) * 16;
+    auto gload2 = [&](Staging2& sg, int kt) __attribute__((always_inline)) {
+        const int soff = kt * BN * HD * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sg.r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs2, voff2[i], soff, 0));
+    };
+    auto lstore2 = [&](const Staging2& sg, int stage) __attribute__((always_inline)) {
+        char* kbuf = smem + (stage * KS + kgp) * L::STAGE;
+        if (v_half) {
+            _Float16* vt = (_Float16*)(kbuf + L::KREG);
+            const int kg = th % (BN / 4), dc = th / (BN / 4);
+            _Float16* dst = vt + (8 * dc) * L::VTP + 4 * kg;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                *(u32x2*)(dst + (2 * j) * L::VTP) =
+                    u32x2{__builtin_amdgcn_perm(sg.r[1][j], sg.r[0][j], 0x05040100u),
+                          __builtin_amdgcn_perm(sg.r[3][j], sg.r[2][j], 0x05040100u)};
+                *(u32x2*)(dst + (2 * j + 1) * L::VTP) =
+                    u32x2{__builtin_amdgcn_perm(sg.r[1][j], sg.r[0][j], 0x07060302u),
+                          __builtin_amdgcn_perm(sg.r[3][j], sg.r[2][j], 0x07060302u)};
+            }
+        } else {
+            _Float16* k16 = (_Float16*)kbuf;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int c = th + n * (NT / 2);
+                *(u32x4*)(k16 + (c / (HD / 8)) * L::KP + (c % (HD / 8)) * 8) = sg.r[n];
+            }
+        }
+    };
+
+    auto gload = [&](Staging& sg, int kt, bool i8) __attribute__((always_inline)) {
+        u32x4(&kreg)[KCH] = sg.kreg;
+        u32x4(&vreg)[VB][4] = sg.vreg;
+        u32x4& skreg = sg.skreg;
         if (ROUTED && i8) {
             const int soff = kt * BN * HD;
 #pragma unroll
@@ -365,8 +433,11 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
         }
     };
 
-    auto lstore = [&](int stage, bool i8) __attribute__((always_inline)) {
-        char* kbuf = smem + stage * L::STAGE;
+    auto lstore = [&](const Staging& sg, int stage, bool i8) __attribute__((always_inline)) {
+        const u32x4(&kreg)[KCH] = sg.kreg;
+        const u32x4(&vreg)[VB][4] = sg.vreg;
+        const u32x4& skreg = sg.skreg;
+        char* kbuf = smem + (stage * KS + kgp) * L::STAGE;
         _Float16* vt = (_Float16*)(kbuf + L::KREG);
         if (ROUTED && i8) {
 #pragma unroll
@@ -424,12 +495,13 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
     const int krow = (lq & ~12) | ((lq & 4) << 1) | ((lq & 8) >> 1);
 
     // One key tile: scores, optional mask, online softmax, P.V.
-    auto tile = [&](auto mask_tag, int kt, bool i8) __attribute__((always_inline)) {
+    auto tile = [&](auto mask_tag, int stage, int kt, bool i8) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const char* kbuf = smem + (kt & 1) * L::STAGE;
+        const char* kbuf = smem + (stage * KS + kgp) * L::STAGE;
         const _Float16* vt = (const _Float16*)(kbuf + L::KREG);
         float x[NKB][16];
         float amul;
+        f16x8 vfr[EARLY ? 2 * NKB : 1][EARLY ? NDB : 1];   // V fragments requested with K
         if (ROUTED && i8) {
             const float* skc = (const float*)(kbuf + BN * L::K8P);
 #pragma unroll
@@ -458,17 +530,46 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
             amul = sq_mul;
         } else {
             const _Float16* k16 = (const _Float16*)kbuf;
+            if constexpr (EARLY) {
+                // every K and V fragment of the tile is requested up front: the
+                // K reads land back to back for the score MFMAs and the V reads
+                // land under the softmax instead of in front of each MFMA
+                f16x8 kfr[NKB][HD / 16];
 #pragma unroll
-            for (int kb32 = 0; kb32 < NKB; ++kb32) {
-                f32x16 acc = f32x16{};
-                const _Float16* kr = k16 + (32 * kb32 + krow) * L::KP + 16 * g;
+                for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
-                for (int t = 0; t < HD / 16; ++t) {
-                    const f16x8 av = *(const f16x8*)(kr + 32 * (t / 2) + 8 * (t % 2));
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[t], acc, 0, 0, 0);
+                    for (int t = 0; t < HD / 16; ++t)
+                        kfr[kb32][t] = *(const f16x8*)(k16 + (32 * kb32 + krow) * L::KP + 16 * g +
+                                                       32 * (t / 2) + 8 * (t % 2));
+                const _Float16* vrow = vt + lq * L::VTP + 8 * g;
+#pragma unroll
+                for (int kk = 0; kk < 2 * NKB; ++kk)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        vfr[kk][db] = *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb32 = 0; kb32 < NKB; ++kb32) {
+                    f32x16 acc = f32x16{};
+#pragma unroll
+                    for (int t = 0; t < HD / 16; ++t)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kfr[kb32][t], qf[t], acc, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) x[kb32][i] = acc[i];
                 }
+            } else {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) x[kb32][i] = acc[i];
+                for (int kb32 = 0; kb32 < NKB; ++kb32) {
+                    f32x16 acc = f32x16{};
+                    const _Float16* kr = k16 + (32 * kb32 + krow) * L::KP + 16 * g;
+#pragma unroll
+                    for (int t = 0; t < HD / 16; ++t) {
+                        const f16x8 av = *(const f16x8*)(kr + 32 * (t / 2) + 8 * (t % 2));
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[t], acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) x[kb32][i] = acc[i];
+                }
             }
             amul = a.c;
         }
@@ -520,7 +621,8 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
         for (int kk = 0; kk < 2 * NKB; ++kk)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const f16x8 av = *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
+                const f16x8 av = (EARLY && !(ROUTED && i8)) ? vfr[kk][db]
+                                                             : *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[kk >> 1][kk & 1], o[db], 0, 0, 0);
             }
     };
@@ -534,31 +636,122 @@ __global__ __launch_bounds__(NW * 64, NW == 2 ? 1 : (BN == 32 ? 3 : 2)) void att
     const int kt0 = min(nkt, split * chunk);
     const int kt1 = min(nkt, kt0 + chunk);
 
-    bool i8_next = ROUTED && kt0 < kt1 && tile_i8(kt0);
-    if (kt0 < kt1) {
-        gload(kt0, i8_next);
-        lstore(kt0 & 1, i8_next);
+    // Iteration it covers tiles kt0 + KS*it .. + KS-1, one per key group; the
+    // first it_full iterations have every tile below nfull.  Tile it of this
+    // group lives in staging set it % PF and LDS stage it % 2.
+    const int n_it = (kt1 - kt0 + KS - 1) / KS;
+    const int it_full = max(0, (min(nfull, kt1) - kt0) / KS);
+    const int kt_first = kt0 + kgp;
+    auto has = [&](int it) __attribute__((always_inline)) { return it < n_it && kt_first + KS * it < kt1; };
+    auto i8_of = [&](int it) __attribute__((always_inline)) {
+        return ROUTED && has(it) && tile_i8(kt_first + KS * it);
+    };
+
+    // Prologue: the first PF tiles' loads go out behind the query loads, and
+    // one wait covers them all.
+    bool i8_c = i8_of(0), i8_n1 = i8_of(1);
+    if constexpr (PF == 2) {
+        gload2(set0, kt_first);
+        gload2(set1, kt_first + KS);
+    } else {
+        if (has(0)) gload(set0, kt_first, i8_c);
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (a.neg) {
+#pragma unroll
+        for (int t = 0; t < HD / 16; ++t) qf[t] = -qf[t];
+    }
+    if constexpr (ROUTED) {
+        float sq;
+        quantize_q_regs<HD>(qf, q8, sq);
+        sq_mul = sq > 0.0f ? sq : 1.0f;   // a zero row has all-zero INT8 scores
+    }
+    if constexpr (PF == 2) lstore2(set0, 0);
+    else if (has(0)) lstore(set0, 0, i8_c);
     __syncthreads();
 
-    int kt = kt0;
-    for (; kt < min(nfull, kt1); ++kt) {
-        const bool i8_cur = i8_next;
-        const bool more = kt + 1 < kt1;
-        i8_next = ROUTED && more && tile_i8(kt + 1);
-        if (more) gload(kt + 1, i8_next);
-        if (wave_active) tile(std::false_type{}, kt, i8_cur);
-        if (more) lstore((kt + 1) & 1, i8_next);
+    const int kt_end = min(w_nkt, kt1);
+    // One iteration; P is the parity of it (selects the staging sets).
+    auto iter = [&](auto mask_tag, auto par_tag, int it) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr int P = decltype(par_tag)::value;
+        const int kt = kt_first + KS * it;
+        const bool i8_cur = i8_c;
+        if constexpr (PF == 2) {
+            // tile it+1 is already in flight (set (it+1)%2); issue tile it+2
+            // into set it%2, which tile it left at its LDS store.  Loads and
+            // stores of tiles past the end are harmless (zeros, into a stage
+            // nobody reads), and keeping them unconditional keeps the load
+            // count that the store of set (it+1)%2 waits for exact.
+            gload2(P == 0 ? set0 : set1, kt + 2 * KS);
+            if (MASK ? kt < kt_end : wave_active) tile(mask_tag, it & 1, kt, false);
+            lstore2(P == 0 ? set1 : set0, (it + 1) & 1);
+        } else {
+            i8_n1 = i8_of(it + 1);
+            if (has(it + 1)) gload(set0, kt + KS, i8_n1);
+            if (MASK ? kt < kt_end : wave_active) tile(mask_tag, it & 1, kt, i8_cur);
+            if (has(it + 1)) lstore(set0, (it + 1) & 1, i8_n1);
+            i8_c = i8_n1;
+        }
         __syncthreads();
-    }
-    for (; kt < kt1; ++kt) {
-        const bool i8_cur = i8_next;
-        const bool more = kt + 1 < kt1;
-        i8_next = ROUTED && more && tile_i8(kt + 1);
-        if (more) gload(kt + 1, i8_next);
-        if (kt < w_nkt) tile(std::true_type{}, kt, i8_cur);
-        if (more) lstore((kt + 1) & 1, i8_next);
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int it = 0;
+    // iterations [it, it_end); with two staging sets the body is unrolled by
+    // two so that each set is a fixed register range
+    auto run = [&](auto mask_tag, int it_end) __attribute__((always_inline)) {
+        if constexpr (PF == 2) {
+            if ((it & 1) && it < it_end) iter(mask_tag, P1{}, it++);
+            for (; it + 1 < it_end; it += 2) {
+                iter(mask_tag, P0{}, it);
+                iter(mask_tag, P1{}, it + 1);
+            }
+            if (it < it_end) iter(mask_tag, P0{}, it++);
+        } else {
+            for (; it < it_end; ++it) iter(mask_tag, P0{}, it);
+        }
+    };
+    run(std::false_type{}, it_full);
+    run(std::true_type{}, n_it);
+
+    if constexpr (KS > 1) {
+        // Merge the key groups' states into group 0 through LDS (every stage
+        // is free after the loop's last barrier).  Lane layouts agree across
+        // groups, so the merge is lane by lane: O = sum_g 2^(m_g - m) O_g,
+        // l likewise, m = max_g m_g.
+        constexpr int NE4 = NDB * 4 + 1;       // f32x4 slots per lane: O, then (m, l)
+        static_assert((KS - 1) * NW * NE4 * 64 * 16 <= L::TOTAL * KS, "merge buffer exceeds LDS");
+        f32x4* xb = (f32x4*)smem;
+        if (kgp > 0) {
+            f32x4* dst = xb + (size_t)((kgp - 1) * NW + w) * NE4 * 64 + l;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(db * 4 + r) * 64] = f32x4{o[db][4 * r], o[db][4 * r + 1], o[db][4 * r + 2], o[db][4 * r + 3]};
+            dst[NDB * 4 * 64] = f32x4{m_run, l_run, 0.0f, 0.0f};
+        }
         __syncthreads();
+        if (kgp > 0) return;
+#pragma unroll
+        for (int j = 1; j < KS; ++j) {
+            const f32x4* src = xb + (size_t)((j - 1) * NW + w) * NE4 * 64 + l;
+            const f32x4 ml = src[NDB * 4 * 64];
+            const float m_new = fmaxf(m_run, ml[0]);
+            const float a0 = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float a1 = __builtin_amdgcn_exp2f(ml[0] - m_new);
+            l_run = l_run * a0 + ml[1] * a1;
+            m_run = m_new;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const f32x4 ov = src[(db * 4 + r) * 64];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[db][4 * r + e] = o[db][4 * r + e] * a0 + ov[e] * a1;
+                }
+        }
     }
 
     // ---- epilogue: O / l -> fp16, or a split partial --------------------------------
@@ -715,32 +908,35 @@ hipError_t set_lds(K kernel, int bytes) {
     return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int HD, int NW, bool CAUSAL, bool VARLEN, bool ROUTED>
+template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED>
 hipError_t launch_fwd_t(const FwdArgs& a, int grid, hipStream_t st) {
-    auto kern = attn_fwd_kernel<HD, NW, CAUSAL, VARLEN, ROUTED>;
-    constexpr int lds = Lds<HD>::TOTAL;
+    auto kern = attn_fwd_kernel<HD, NW, KS, CAUSAL, VARLEN, ROUTED>;
+    constexpr int lds = Lds<HD>::TOTAL * KS;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * KS * 64), lds, st, a);
     return hipGetLastError();
 }
 
-template <int HD, int NW>
+template <int HD, int NW, int KS>
 hipError_t dispatch_flags(const FwdArgs& a, int grid, bool causal, bool varlen, bool routed,
                           hipStream_t st) {
     if (routed) {
-        if (varlen)
-            return causal ? launch_fwd_t<HD, NW, true, true, true>(a, grid, st)
-                          : launch_fwd_t<HD, NW, false, true, true>(a, grid, st);
-        return causal ? launch_fwd_t<HD, NW, true, false, true>(a, grid, st)
-                      : launch_fwd_t<HD, NW, false, false, true>(a, grid, st);
+        if constexpr (KS == 1) {
+            if (varlen)
+                return causal ? launch_fwd_t<HD, NW, KS, true, true, true>(a, grid, st)
+                              : launch_fwd_t<HD, NW, KS, false, true, true>(a, grid, st);
+            return causal ? launch_fwd_t<HD, NW, KS, true, false, true>(a, grid, st)
+                          : launch_fwd_t<HD, NW, KS, false, false, true>(a, grid, st);
+        }
+        return hipErrorInvalidConfiguration;   // routed calls use one key group
     }
     if constexpr (NW == 4) {
         if (varlen)
-            return causal ? launch_fwd_t<HD, NW, true, true, false>(a, grid, st)
-                          : launch_fwd_t<HD, NW, false, true, false>(a, grid, st);
-        return causal ? launch_fwd_t<HD, NW, true, false, false>(a, grid, st)
-                      : launch_fwd_t<HD, NW, false, false, false>(a, grid, st);
+            return causal ? launch_fwd_t<HD, NW, KS, true, true, false>(a, grid, st)
+                          : launch_fwd_t<HD, NW, KS, false, true, false>(a, grid, st);
+        return causal ? launch_fwd_t<HD, NW, KS, true, false, false>(a, grid, st)
+                      : launch_fwd_t<HD, NW, KS, false, false, false>(a, grid, st);
     }
     return hipErrorInvalidConfiguration;   // two-wave workgroups exist for routed calls only
 }
@@ -805,7 +1001,7 @@ static int largest_div(int G, int cap) {
 
 // Launch plan of one forward call: workgroup shape, key splits, scratch layout.
 struct Plan {
-    int NW, HPW, BM, combos, n_mblk, ksplit;
+    int NW, KS, HPW, BM, combos, n_mblk, ksplit;
     long long grid;
     size_t k8_off, sk_off, po_off, pl_off, bytes;   // scratch layout (bytes)
     long long out_rows;
@@ -825,15 +1021,22 @@ static Plan make_plan(const Problem& p) {
     pl.BM = (pl.NW / pl.HPW) * 32;
     pl.combos = (varlen ? 1 : p.B) * p.n_kvh * (G / pl.HPW);
     pl.n_mblk = varlen ? (p.qsl + pl.BM - 1) / pl.BM + p.B : (p.qsl + pl.BM - 1) / pl.BM;
-    // Split the key range when the grid leaves SIMDs without a wavefront (the
-    // partials and their merge cost more than they return otherwise): up to
-    // two wavefronts per SIMD, keeping at least eight tiles per split.
+    // Small grids leave SIMDs with one wavefront or none, so nothing hides
+    // the latency of one wavefront's loads, softmax and MFMA chains.  First
+    // give each workgroup a second key group (same rows, alternate key tiles,
+    // merged in LDS); then, if SIMDs are still idle, split the key range over
+    // workgroups (fp32 partials and a merge pass, which cost more than they
+    // return otherwise): up to two wavefronts per SIMD, keeping at least
+    // sixteen tiles per split.
     const long long waves = (long long)pl.combos * pl.n_mblk * pl.NW;
     const long long simds = 4LL * cu_count();
     const int n_kt = (p.ksl + BN - 1) / BN;
+    pl.KS = (!routed && pl.NW == 4 && waves < 2 * simds && n_kt >= 2) ? 2 : 1;
+    const char* force_kg = getenv("ATTN_KEY_GROUPS");
+    if (!routed && pl.NW == 4 && force_kg && (force_kg[0] == '1' || force_kg[0] == '2') && force_kg[1] == 0)
+        pl.KS = force_kg[0] - '0';
     int ks = 1;
-    if (waves < simds)
-        while (ks < 8 && waves * ks < 2 * simds && n_kt >= 16 * ks) ks *= 2;
+    while (ks < 8 && waves * pl.KS * ks < 2 * simds && n_kt >= 16 * ks) ks *= 2;
     const char* force = getenv("ATTN_KSPLIT");
     if (force && force[0] >= '1' && force[0] <= '8' && force[1] == 0) ks = force[0] - '0';
     pl.ksplit = ks;
@@ -907,11 +1110,13 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
     const int grid = (int)pl.grid;
     hipError_t e;
     if (p.hdim == 64)
-        e = pl.NW == 4 ? dispatch_flags<64, 4>(a, grid, p.causal, varlen, routed, st)
-                       : dispatch_flags<64, 2>(a, grid, p.causal, varlen, routed, st);
+        e = pl.NW == 2   ? dispatch_flags<64, 2, 1>(a, grid, p.causal, varlen, routed, st)
+            : pl.KS == 1 ? dispatch_flags<64, 4, 1>(a, grid, p.causal, varlen, routed, st)
+                         : dispatch_flags<64, 4, 2>(a, grid, p.causal, varlen, routed, st);
     else
-        e = pl.NW == 4 ? dispatch_flags<128, 4>(a, grid, p.causal, varlen, routed, st)
-                       : dispatch_flags<128, 2>(a, grid, p.causal, varlen, routed, st);
+        e = pl.NW == 2   ? dispatch_flags<128, 2, 1>(a, grid, p.causal, varlen, routed, st)
+            : pl.KS == 1 ? dispatch_flags<128, 4, 1>(a, grid, p.causal, varlen, routed, st)
+                         : dispatch_flags<128, 4, 2>(a, grid, p.causal, varlen, routed, st);
     if (e != hipSuccess || pl.ksplit == 1) return e;
     const long long threads = pl.out_rows * (p.hdim / 8);
     const int mgrid = (int)((threads + 255) / 256);

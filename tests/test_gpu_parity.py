@@ -70,16 +70,25 @@ def rand16(rng, shape):
 SHAPES = [(1, 1), (5, 70), (64, 64), (65, 65), (130, 130), (200, 333), (333, 200), (300, 1000)]
 
 
+@pytest.fixture(params=["1", "2"], ids=["kg1", "kg2"])
+def key_groups(request, monkeypatch):
+    """Both workgroup shapes of non-routed calls: one key group, or two key
+    groups that take alternate key tiles and merge in LDS (what small grids
+    get by default)."""
+    monkeypatch.setenv("ATTN_KEY_GROUPS", request.param)
+    return int(request.param)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("heads", [(3, 3), (4, 2), (8, 2), (8, 1)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_dense_ragged(A, orc, d, heads, causal):
+def test_dense_ragged(A, orc, d, heads, causal, key_groups):
     rng = np.random.default_rng(d * 100 + heads[0] * 10 + heads[1] + causal)
     for (qsl, ksl) in SHAPES:
         if causal and qsl > ksl:
             continue
         B = 2 if qsl <= 70 else 1
-        say("dense d=%d heads=%s causal=%d B=%d qsl=%d ksl=%d" % (d, heads, causal, B, qsl, ksl))
+        say("dense d=%d heads=%s causal=%d B=%d qsl=%d ksl=%d kg=%d" % (d, heads, causal, B, qsl, ksl, key_groups))
         q, k, v = rand16(rng, (B, heads[0], qsl, d)), rand16(rng, (B, heads[1], ksl, d)), \
             rand16(rng, (B, heads[1], ksl, d))
         scale = float(np.float32(1 / np.sqrt(d)))
@@ -91,12 +100,12 @@ def test_dense_ragged(A, orc, d, heads, causal):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("heads", [(2, 2), (8, 2)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_varlen_ragged(A, orc, d, heads, causal):
+def test_varlen_ragged(A, orc, d, heads, causal, key_groups):
     rng = np.random.default_rng(7 + d + heads[1] + causal)
     lens = [1, 63, 64, 65, 200, 0, 130, 7]
     cu = W.cu_seqlens_of(lens)
     T = int(cu[-1])
-    say("varlen d=%d heads=%s causal=%d lens=%s" % (d, heads, causal, lens))
+    say("varlen d=%d heads=%s causal=%d lens=%s kg=%d" % (d, heads, causal, lens, key_groups))
     q, k, v = rand16(rng, (heads[0], T, d)), rand16(rng, (heads[1], T, d)), rand16(rng, (heads[1], T, d))
     got = gpu_attn(A, q, k, v, 0.1, causal, cu=cu)
     ref = orc.attn_fwd(q, k, v, scale=0.1, causal=causal, cu_seqlens=cu)
@@ -142,7 +151,9 @@ def test_routed_varlen_ragged(A, orc, d, heads, causal, tpb):
     check(got, ref)
 
 
-def test_gpu_routed_varlen_zero_mask_is_dense(A):
+def test_gpu_routed_varlen_zero_mask_is_dense(A, monkeypatch):
+    """Routed calls run one key group; the dense call is pinned to the same shape."""
+    monkeypatch.setenv("ATTN_KEY_GROUPS", "1")
     rng = np.random.default_rng(510)
     lens = [100, 1, 250, 64]
     cu = W.cu_seqlens_of(lens)
@@ -217,7 +228,9 @@ def test_gpu_rows_sum_to_one(A, routed):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_gpu_all_zero_mask_is_dense_bitexact(A, d):
+def test_gpu_all_zero_mask_is_dense_bitexact(A, d, monkeypatch):
+    """Routed calls run one key group; the dense call is pinned to the same shape."""
+    monkeypatch.setenv("ATTN_KEY_GROUPS", "1")
     rng = np.random.default_rng(63)
     q, k, v = rand16(rng, (1, 8, 300, d)), rand16(rng, (1, 2, 300, d)), rand16(rng, (1, 2, 300, d))
     zeros = W.pack_bits(np.zeros((5, 2), dtype=bool))
@@ -227,8 +240,10 @@ def test_gpu_all_zero_mask_is_dense_bitexact(A, d):
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
-def test_gpu_varlen_equals_separate_calls(A, monkeypatch):
-    """Same tiling (no key split): bit-identical; default launch plans: within fp16 rounding."""
+@pytest.mark.parametrize("kg", ["1", "2"])
+def test_gpu_varlen_equals_separate_calls(A, monkeypatch, kg):
+    """Same tiling (fixed key groups, no split over workgroups): bit-identical;
+    default launch plans: within fp16 rounding."""
     rng = np.random.default_rng(64)
     lens = [70, 1, 129, 300]
     cu = W.cu_seqlens_of(lens)
@@ -236,6 +251,7 @@ def test_gpu_varlen_equals_separate_calls(A, monkeypatch):
     q, k, v = rand16(rng, (8, T, 128)), rand16(rng, (2, T, 128)), rand16(rng, (2, T, 128))
     packed = gpu_attn(A, q, k, v, 0.1, True, cu=cu)
     monkeypatch.setenv("ATTN_KSPLIT", "1")
+    monkeypatch.setenv("ATTN_KEY_GROUPS", kg)
     packed1 = gpu_attn(A, q, k, v, 0.1, True, cu=cu)
     for s in range(len(lens)):
         a, b = cu[s], cu[s + 1]
