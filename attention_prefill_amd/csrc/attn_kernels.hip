@@ -585,6 +585,20 @@ void attn_fwd_kernel(FwdArgs a) {
                     if (kl + 32 * kb32 + (i % 8) + 16 * (i / 8) > lim) x[kb32][i] = -INFINITY;
         }
 
+        // O^T += V^T P^T over the two 16-key steps of one 32-key block
+        const _Float16* vrow = vt + lq * L::VTP + 8 * g;
+        auto pv = [&](int kb32, const f16x8(&pkb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int kk = 2 * kb32 + t;
+                    const f16x8 av = (EARLY && !(ROUTED && i8)) ? vfr[kk][db]
+                                                                 : *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pkb[t], o[db], 0, 0, 0);
+                }
+        };
+
         // online softmax in base 2 with a lazily moved reference max
         float mt = -INFINITY;
 #pragma unroll
@@ -606,25 +620,17 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb32][8 * t + j], amul, nm));
                     rs += p;
                     pk[kb32][t][j] = (_Float16)p;
                 }
-        l_run += rs;
-
-        // O^T += V^T P^T over the 16-key steps of the tile
-        const _Float16* vrow = vt + lq * L::VTP + 8 * g;
-#pragma unroll
-        for (int kk = 0; kk < 2 * NKB; ++kk)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const f16x8 av = (EARLY && !(ROUTED && i8)) ? vfr[kk][db]
-                                                             : *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pk[kk >> 1][kk & 1], o[db], 0, 0, 0);
             }
+        l_run += rs;
+#pragma unroll
+        for (int kb32 = 0; kb32 < NKB; ++kb32) pv(kb32, pk[kb32]);
     };
 
     // Tiles [0, nfull) are fully visible to every row of the workgroup; the

@@ -48,6 +48,12 @@
  *    in sequence order; row r0(s) = sum over s' < s of ceil(L_s'/tile_q).
  *    All rows have wpr words for the packed length T; bits of groups past a
  *    sequence's own key tiles are never read.
+ *  - INT8 key/value caches (oracle_attn_fwd_kv8): K and V arrive as INT8
+ *    codes with one fp32 scale per row, made by the same quantiser; the
+ *    keys and values they stand for are K^ = s_k * k8 and V^ = s_v * v8.
+ *    FP16 cells take the fp16 query against K^; INT8 cells take the
+ *    quantised query against the cached codes (no second quantisation of
+ *    K^); the output weights V^.
  *  - Output is the exact fp64 result; a fp16 round-to-nearest-even encoder
  *    is provided for exact special cases.
  *
@@ -141,6 +147,13 @@ void oracle_quantize_row(const uint16_t* x, int d, int8_t* q8, float* s_out)
 /* of adjacent key tiles).                                                 */
 /* ---------------------------------------------------------------------- */
 
+/* Every row of an [rows, d] fp16 array, by oracle_quantize_row. */
+void oracle_quantize_rows(const uint16_t* x, long long rows, int d, int8_t* q8, float* s_out)
+{
+    for (long long r = 0; r < rows; ++r)
+        oracle_quantize_row(x + (size_t)r * d, d, q8 + (size_t)r * d, s_out + r);
+}
+
 int oracle_route_words_per_row(int ksl, int tile_k, int tiles_per_bit)
 {
     int n_kt = (ksl + tile_k - 1) / tile_k;
@@ -159,6 +172,9 @@ int oracle_route_bit(const uint32_t* words, int wpr, int qt, int g)
 
 typedef struct {
     const uint16_t *q, *k, *v;
+    /* INT8 key/value cache mode (k and v unused): codes and per-row scales */
+    const int8_t *k8, *v8;
+    const float *sk, *sv;
     int B, qsl, ksl, d, n_qh, n_kvh, causal;
     double scale;
     const int32_t* cu;
@@ -208,6 +224,20 @@ static int visible(const problem* p, int i, int j, int Lq, int Lk)
     return !p->causal || j <= i + (Lk - Lq);
 }
 
+/* Value t of key / value row j of the slab starting at element kb: the fp16
+ * tensor's value, or in cache mode the dequantised s * code (exact in fp64). */
+static double key_val(const problem* p, size_t kb, int j, int t)
+{
+    if (p->k8) return (double)p->sk[kb / p->d + j] * (double)p->k8[kb + (size_t)j * p->d + t];
+    return oracle_f16_to_f64(p->k[kb + (size_t)j * p->d + t]);
+}
+
+static double val_val(const problem* p, size_t kb, int j, int t)
+{
+    if (p->v8) return (double)p->sv[kb / p->d + j] * (double)p->v8[kb + (size_t)j * p->d + t];
+    return oracle_f16_to_f64(p->v[kb + (size_t)j * p->d + t]);
+}
+
 /* Quantised rows for one (s, head) slab of L rows, or NULL when unrouted. */
 typedef struct { int8_t* q8; float* s; } qrows;
 
@@ -224,15 +254,30 @@ static qrows quantize_slab(const problem* p, const uint16_t* base, int L)
 
 static void free_qrows(qrows r) { free(r.q8); free(r.s); }
 
+/* INT8 K rows of the slab starting at element kb: quantised from the fp16
+ * keys, or in cache mode the cached codes and scales themselves. */
+static qrows key_codes(const problem* p, size_t kb, int L)
+{
+    if (p->k8) {
+        qrows r = { NULL, NULL };
+        if (!p->route || L == 0) return r;
+        r.q8 = (int8_t*)malloc((size_t)L * p->d);
+        r.s = (float*)malloc((size_t)L * sizeof(float));
+        memcpy(r.q8, p->k8 + kb, (size_t)L * p->d);
+        memcpy(r.s, p->sk + kb / p->d, (size_t)L * sizeof(float));
+        return r;
+    }
+    return quantize_slab(p, p->k + kb, L);
+}
+
 /* Scores of query row i against all Lk keys; masked cells get -inf. */
-static void score_row(const problem* p, const uint16_t* qrow, const uint16_t* kb,
+static void score_row(const problem* p, const uint16_t* qrow, size_t kb,
                       const qrows* qq, const qrows* kq, int i, int Lq, int Lk, int rrow0,
                       double* S)
 {
     int qt = rrow0 + i / p->tile_q;
     for (int j = 0; j < Lk; ++j) {
         if (!visible(p, i, j, Lq, Lk)) { S[j] = -INFINITY; continue; }
-        const uint16_t* krow = kb + (size_t)j * p->d;
         int int8_cell = 0;
         if (p->route) {
             int g = (j / p->tile_k) / p->tiles_per_bit;
@@ -245,16 +290,17 @@ static void score_row(const problem* p, const uint16_t* qrow, const uint16_t* kb
             for (int t = 0; t < p->d; ++t) dot += (int64_t)a[t] * (int64_t)b[t];
             S[j] = p->scale * (double)qq->s[i] * (double)kq->s[j] * (double)dot;
         } else {
-            double acc = 0.0;   /* fp16 x fp16 products are exact in fp64 */
+            /* fp16 x fp16 and fp16 x (fp32 * int8) products are exact in fp64 */
+            double acc = 0.0;
             for (int t = 0; t < p->d; ++t)
-                acc += oracle_f16_to_f64(qrow[t]) * oracle_f16_to_f64(krow[t]);
+                acc += oracle_f16_to_f64(qrow[t]) * key_val(p, kb, j, t);
             S[j] = p->scale * acc;
         }
     }
 }
 
 /* In-place row softmax over Lk cells (base e), then out = P . V. */
-static void softmax_pv_row(const problem* p, double* S, int Lk, const uint16_t* vb, double* out)
+static void softmax_pv_row(const problem* p, double* S, int Lk, size_t kb, double* out)
 {
     double m = -INFINITY;
     for (int j = 0; j < Lk; ++j) if (S[j] > m) m = S[j];
@@ -267,14 +313,14 @@ static void softmax_pv_row(const problem* p, double* S, int Lk, const uint16_t* 
     for (int j = 0; j < Lk; ++j) {
         if (S[j] == 0.0) continue;
         double pj = S[j] / l;
-        const uint16_t* vrow = vb + (size_t)j * p->d;
-        for (int t = 0; t < p->d; ++t) out[t] += pj * oracle_f16_to_f64(vrow[t]);
+        for (int t = 0; t < p->d; ++t) out[t] += pj * val_val(p, kb, j, t);
     }
 }
 
 static int check_problem(const problem* p)
 {
-    if (!p->q || !p->k || !p->v) return ORACLE_ERR_ARG;
+    if (!p->q) return ORACLE_ERR_ARG;
+    if (p->k8 ? (!p->v8 || !p->sk || !p->sv) : (!p->k || !p->v)) return ORACLE_ERR_ARG;
     if (p->B <= 0 || p->qsl <= 0 || p->ksl <= 0 || p->d <= 0 || p->n_qh <= 0 || p->n_kvh <= 0)
         return ORACLE_ERR_ARG;
     if (p->n_qh % p->n_kvh) return ORACLE_ERR_ARG;
@@ -294,6 +340,7 @@ static problem make_problem(const uint16_t* q, const uint16_t* k, const uint16_t
 {
     problem p;
     p.q = q; p.k = k; p.v = v;
+    p.k8 = NULL; p.v8 = NULL; p.sk = NULL; p.sv = NULL;
     p.B = B; p.qsl = qsl; p.ksl = ksl; p.d = d; p.n_qh = n_qh; p.n_kvh = n_kvh;
     p.causal = causal ? 1 : 0;
     p.scale = (double)scale;                 /* caller's fp32 scale, widened */
@@ -305,14 +352,10 @@ static problem make_problem(const uint16_t* q, const uint16_t* k, const uint16_t
     return p;
 }
 
-int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* out,
-                    int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
-                    float scale, int causal, const int32_t* cu_seqlens,
-                    const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
-                    int nthreads)
+static int run_fwd(problem p, double* out, int nthreads)
 {
-    problem p = make_problem(q, k, v, B, qsl, ksl, d, n_qh, n_kvh, scale, causal,
-                             cu_seqlens, route, tiles_per_bit, tile_q, tile_k);
+    const uint16_t* q = p.q;
+    const int B = p.B, d = p.d, n_qh = p.n_qh, n_kvh = p.n_kvh;
     int rc = check_problem(&p);
     if (rc) return rc;
     if (!out) return ORACLE_ERR_ARG;
@@ -329,7 +372,7 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, dou
         for (int hk = 0; hk < n_kvh; ++hk) {
             int Lk;
             size_t kb = kv_base(&p, s, hk, &Lk);
-            qrows kq = quantize_slab(&p, k + kb, Lk);
+            qrows kq = key_codes(&p, kb, Lk);
             for (int h = hk * G; h < (hk + 1) * G; ++h) {
                 int Lq;
                 size_t qb = q_base(&p, s, h, &Lq);
@@ -342,13 +385,13 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, dou
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
 #endif
                 for (int i = 0; i < Lq; ++i)
-                    score_row(&p, q + qb + (size_t)i * d, k + kb, &qq, &kq, i, Lq, Lk, rrow0,
+                    score_row(&p, q + qb + (size_t)i * d, kb, &qq, &kq, i, Lq, Lk, rrow0,
                               S + (size_t)i * Lk);
 #ifdef _OPENMP
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nt)
 #endif
                 for (int i = 0; i < Lq; ++i)
-                    softmax_pv_row(&p, S + (size_t)i * Lk, Lk, v + kb, out + qb + (size_t)i * d);
+                    softmax_pv_row(&p, S + (size_t)i * Lk, Lk, kb, out + qb + (size_t)i * d);
                 free(S);
                 free_qrows(qq);
             }
@@ -359,14 +402,10 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, dou
     return 0;
 }
 
-int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                     int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
-                     float scale, int causal, const int32_t* cu_seqlens,
-                     const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
-                     const int32_t* rows, int nrows, double* out, int nthreads)
+static int run_rows(problem p, const int32_t* rows, int nrows, double* out, int nthreads)
 {
-    problem p = make_problem(q, k, v, B, qsl, ksl, d, n_qh, n_kvh, scale, causal,
-                             cu_seqlens, route, tiles_per_bit, tile_q, tile_k);
+    const uint16_t* q = p.q;
+    const int B = p.B, d = p.d, n_qh = p.n_qh, n_kvh = p.n_kvh;
     int rc = check_problem(&p);
     if (rc) return rc;
     if (!out || !rows || nrows < 0) return ORACLE_ERR_ARG;
@@ -400,7 +439,7 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
             qq.q8 = (int8_t*)malloc((size_t)(i + 1) * d);
             qq.s = (float*)malloc((size_t)(i + 1) * sizeof(float));
             oracle_quantize_row(q + qb + (size_t)i * d, d, qq.q8 + (size_t)i * d, qq.s + i);
-            kq = quantize_slab(&p, k + kb, Lk);
+            kq = key_codes(&p, kb, Lk);
         }
         double* S = (double*)malloc((size_t)(Lk > 0 ? Lk : 1) * sizeof(double));
         if (!S) {
@@ -409,8 +448,8 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 #endif
             err = ORACLE_ERR_NOMEM;
         } else {
-            score_row(&p, q + qb + (size_t)i * d, k + kb, &qq, &kq, i, Lq, Lk, route_row0(&p, s), S);
-            softmax_pv_row(&p, S, Lk, v + kb, out + (size_t)r * d);
+            score_row(&p, q + qb + (size_t)i * d, kb, &qq, &kq, i, Lq, Lk, route_row0(&p, s), S);
+            softmax_pv_row(&p, S, Lk, kb, out + (size_t)r * d);
             free(S);
         }
         free_qrows(qq);
@@ -418,4 +457,67 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     }
     fesetround(fe);
     return err;
+}
+
+int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* out,
+                    int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                    float scale, int causal, const int32_t* cu_seqlens,
+                    const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                    int nthreads)
+{
+    return run_fwd(make_problem(q, k, v, B, qsl, ksl, d, n_qh, n_kvh, scale, causal,
+                                cu_seqlens, route, tiles_per_bit, tile_q, tile_k),
+                   out, nthreads);
+}
+
+int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                     float scale, int causal, const int32_t* cu_seqlens,
+                     const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                     const int32_t* rows, int nrows, double* out, int nthreads)
+{
+    return run_rows(make_problem(q, k, v, B, qsl, ksl, d, n_qh, n_kvh, scale, causal,
+                                 cu_seqlens, route, tiles_per_bit, tile_q, tile_k),
+                    rows, nrows, out, nthreads);
+}
+
+/* INT8 key/value cache ("INT8 key/value caches", TileMix abstract): K and V
+ * arrive as per-token INT8 codes with fp32 scales, K^ = s_k * k8 and
+ * V^ = s_v * v8.  FP16 cells score the fp16 query against K^, INT8 cells use
+ * the cached codes as the key side of the integer dot product, and the
+ * output weights V^. */
+static problem make_problem_kv8(const uint16_t* q, const int8_t* k8, const float* sk,
+                                const int8_t* v8, const float* sv,
+                                int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                                float scale, int causal, const int32_t* cu,
+                                const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k)
+{
+    problem p = make_problem(q, NULL, NULL, B, qsl, ksl, d, n_qh, n_kvh, scale, causal,
+                             cu, route, tiles_per_bit, tile_q, tile_k);
+    p.k8 = k8; p.sk = sk; p.v8 = v8; p.sv = sv;
+    return p;
+}
+
+int oracle_attn_fwd_kv8(const uint16_t* q, const int8_t* k8, const float* k_scale,
+                        const int8_t* v8, const float* v_scale, double* out,
+                        int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                        float scale, int causal, const int32_t* cu_seqlens,
+                        const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                        int nthreads)
+{
+    return run_fwd(make_problem_kv8(q, k8, k_scale, v8, v_scale, B, qsl, ksl, d, n_qh, n_kvh,
+                                    scale, causal, cu_seqlens, route, tiles_per_bit, tile_q, tile_k),
+                   out, nthreads);
+}
+
+int oracle_attn_rows_kv8(const uint16_t* q, const int8_t* k8, const float* k_scale,
+                         const int8_t* v8, const float* v_scale,
+                         int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                         float scale, int causal, const int32_t* cu_seqlens,
+                         const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                         const int32_t* rows, int nrows, double* out, int nthreads)
+{
+    return run_rows(make_problem_kv8(q, k8, k_scale, v8, v_scale, B, qsl, ksl, d, n_qh, n_kvh,
+                                     scale, causal, cu_seqlens, route, tiles_per_bit, tile_q, tile_k),
+                    rows, nrows, out, nthreads);
 }

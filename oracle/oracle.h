@@ -25,6 +25,9 @@ uint16_t oracle_f64_to_f16_rne(double x);
 /* q8[0..d) and the fp32 scale s of one row x[0..d) of fp16 bits. */
 void oracle_quantize_row(const uint16_t* x, int d, int8_t* q8, float* s_out);
 
+/* Every row of an [rows, d] fp16 array (the INT8 key/value cache encoder). */
+void oracle_quantize_rows(const uint16_t* x, long long rows, int d, int8_t* q8, float* s_out);
+
 int oracle_route_words_per_row(int ksl, int tile_k, int tiles_per_bit);
 int oracle_route_bit(const uint32_t* words, int wpr, int qt, int g);
 
@@ -43,6 +46,24 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      float scale, int causal, const int32_t* cu_seqlens,
                      const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
                      const int32_t* rows, int nrows, double* out, int nthreads);
+
+/* INT8 key/value cache inputs: k8, v8 int8 in the layout of k, v; k_scale,
+ * v_scale fp32 per row ([B, n_kvh, ksl] or [n_kvh, T]).  The keys and
+ * values are K^ = k_scale * k8 and V^ = v_scale * v8; INT8 routed cells use
+ * k8 and k_scale as the key codes. */
+int oracle_attn_fwd_kv8(const uint16_t* q, const int8_t* k8, const float* k_scale,
+                        const int8_t* v8, const float* v_scale, double* out,
+                        int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                        float scale, int causal, const int32_t* cu_seqlens,
+                        const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                        int nthreads);
+
+int oracle_attn_rows_kv8(const uint16_t* q, const int8_t* k8, const float* k_scale,
+                         const int8_t* v8, const float* v_scale,
+                         int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                         float scale, int causal, const int32_t* cu_seqlens,
+                         const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                         const int32_t* rows, int nrows, double* out, int nthreads);
 
 #ifdef __cplusplus
 }

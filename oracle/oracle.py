@@ -31,6 +31,8 @@ def _load():
         lib.oracle_f64_to_f16_rne.restype = ctypes.c_uint16
         lib.oracle_quantize_row.argtypes = [_P, _I, _P, _P]
         lib.oracle_quantize_row.restype = None
+        lib.oracle_quantize_rows.argtypes = [_P, ctypes.c_longlong, _I, _P, _P]
+        lib.oracle_quantize_rows.restype = None
         lib.oracle_route_words_per_row.argtypes = [_I, _I, _I]
         lib.oracle_route_words_per_row.restype = _I
         lib.oracle_route_bit.argtypes = [_P, _I, _I, _I]
@@ -41,6 +43,11 @@ def _load():
         lib.oracle_attn_fwd.restype = _I
         lib.oracle_attn_rows.argtypes = common + shape + [_P, _I, _P, _I]
         lib.oracle_attn_rows.restype = _I
+        cache = [_P, _P, _P, _P, _P]
+        lib.oracle_attn_fwd_kv8.argtypes = cache + [_P] + shape + [_I]
+        lib.oracle_attn_fwd_kv8.restype = _I
+        lib.oracle_attn_rows_kv8.argtypes = cache + shape + [_P, _I, _P, _I]
+        lib.oracle_attn_rows_kv8.restype = _I
         _lib = lib
     return _lib
 
@@ -139,4 +146,60 @@ def attn_rows(q, k, v, rows, *, scale, causal=False, cu_seqlens=None, route=None
                                   r.shape[0], _ptr(out), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_attn_rows rejected its arguments (code %d)" % rc)
+    return out
+
+
+def quantize_rows(x: np.ndarray):
+    """(codes int8, scales float32) of every last-axis row of an fp16 array:
+    the INT8 key/value cache encoding (same rule as quantize_row)."""
+    xb = _bits(x)
+    d = xb.shape[-1]
+    rows = xb.size // d
+    q8 = np.zeros(xb.shape, dtype=np.int8)
+    s = np.zeros(xb.shape[:-1], dtype=np.float32)
+    _load().oracle_quantize_rows(_ptr(xb), rows, d, _ptr(q8), _ptr(s))
+    return q8, s
+
+
+def _cache(q, k8, k_scale, v8, v_scale, cu_seqlens, route):
+    qb = _bits(q)
+    k8 = np.ascontiguousarray(k8, dtype=np.int8)
+    v8 = np.ascontiguousarray(v8, dtype=np.int8)
+    ks = np.ascontiguousarray(k_scale, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+    assert k8.shape == v8.shape and ks.shape == vs.shape == k8.shape[:-1]
+    cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    rt = None if route is None else np.ascontiguousarray(route, dtype=np.uint32)
+    return qb, k8, ks, v8, vs, cu, rt
+
+
+def attn_fwd_kv8(q, k8, k_scale, v8, v_scale, *, scale, causal=False, cu_seqlens=None, route=None,
+                 tiles_per_bit=4, tile_q=64, tile_k=64, nthreads=0) -> np.ndarray:
+    """Exact fp64 output with INT8 key/value cache inputs (K^ = k_scale * k8,
+    V^ = v_scale * v8), same shape as q."""
+    qb, k8, ks, v8, vs, cu, rt = _cache(q, k8, k_scale, v8, v_scale, cu_seqlens, route)
+    B, qsl, ksl, d, n_qh, n_kvh = _shape_args(qb, k8, cu)
+    out = np.zeros(qb.shape, dtype=np.float64)
+    rc = _load().oracle_attn_fwd_kv8(_ptr(qb), _ptr(k8), _ptr(ks), _ptr(v8), _ptr(vs), _ptr(out),
+                                     B, qsl, ksl, d, n_qh, n_kvh, float(np.float32(scale)),
+                                     int(bool(causal)), _ptr(cu), _ptr(rt), int(tiles_per_bit),
+                                     int(tile_q), int(tile_k), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attn_fwd_kv8 rejected its arguments (code %d)" % rc)
+    return out
+
+
+def attn_rows_kv8(q, k8, k_scale, v8, v_scale, rows, *, scale, causal=False, cu_seqlens=None,
+                  route=None, tiles_per_bit=4, tile_q=64, tile_k=64, nthreads=0) -> np.ndarray:
+    """attn_fwd_kv8 output rows for the (s, h, i) triples in rows, float64 [len(rows), d]."""
+    qb, k8, ks, v8, vs, cu, rt = _cache(q, k8, k_scale, v8, v_scale, cu_seqlens, route)
+    B, qsl, ksl, d, n_qh, n_kvh = _shape_args(qb, k8, cu)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+    out = np.zeros((r.shape[0], d), dtype=np.float64)
+    rc = _load().oracle_attn_rows_kv8(_ptr(qb), _ptr(k8), _ptr(ks), _ptr(v8), _ptr(vs), B, qsl, ksl,
+                                      d, n_qh, n_kvh, float(np.float32(scale)), int(bool(causal)),
+                                      _ptr(cu), _ptr(rt), int(tiles_per_bit), int(tile_q),
+                                      int(tile_k), _ptr(r), r.shape[0], _ptr(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attn_rows_kv8 rejected its arguments (code %d)" % rc)
     return out
