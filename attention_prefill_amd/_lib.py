@@ -49,6 +49,13 @@ def load():
         lib.attn_debug_quantize_rows.restype = _I
         lib.attn_debug_route_dump.argtypes = [_P, _I, _I, _I, _I, _P, _P]
         lib.attn_debug_route_dump.restype = _I
+        kv8_args = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I]
+        lib.attn_fwd_kv8.argtypes = kv8_args
+        lib.attn_fwd_kv8.restype = _I
+        lib.attn_fwd_kv8_stream.argtypes = kv8_args + [_P]
+        lib.attn_fwd_kv8_stream.restype = _I
+        lib.attn_quantize_rows.argtypes = [_P, ctypes.c_int64, _I, _P, _P, _P]
+        lib.attn_quantize_rows.restype = _I
         _lib = lib
     return _lib
 
@@ -96,21 +103,8 @@ def attn_fwd_stream(q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal,
                                   _ptr(route_bitmask), int(tiles_per_bit), _stream(stream)))
 
 
-def attn_fwd(q, k, v, out=None, *, scale=None, causal=False, cu_seqlens=None,
-             route_bitmask=None, tiles_per_bit=4, stream=None):
-    """Fused attention forward; sizes are read from the tensor shapes.
-
-    dense:  q [B, n_qh, qsl, d], k/v [B, n_kvh, ksl, d]
-    packed: q [n_qh, T, d], k/v [n_kvh, T, d], cu_seqlens int32 [B + 1]
-    route_bitmask: int32 / uint32-valued tensor of packed routing words.
-    Returns out (allocated when None).  Enqueued on torch's current stream.
-    """
+def _shapes(q, k, cu_seqlens):
     import torch
-    _need(q, "q", torch.float16)
-    _need(k, "k", torch.float16)
-    _need(v, "v", torch.float16)
-    if k.shape != v.shape:
-        raise ValueError("k and v must have the same shape")
     if cu_seqlens is None:
         if q.dim() != 4 or k.dim() != 4:
             raise ValueError("dense q/k/v must be 4-D [B, H, S, d]")
@@ -127,16 +121,40 @@ def attn_fwd(q, k, v, out=None, *, scale=None, causal=False, cu_seqlens=None,
         B = cu_seqlens.numel() - 1
     if dk != d:
         raise ValueError("q and k head dims differ")
+    return B, qsl, ksl, d, n_qh, n_kvh
+
+
+def _out_route(q, out, route_bitmask):
+    import torch
     if route_bitmask is not None:
         if route_bitmask.dtype not in (torch.int32, torch.uint32):
             raise TypeError("route_bitmask must hold 32-bit words")
         _need(route_bitmask, "route_bitmask", route_bitmask.dtype)
     if out is None:
-        out = torch.empty_like(q)
-    else:
-        _need(out, "out", torch.float16)
-        if out.shape != q.shape:
-            raise ValueError("out must have q's shape")
+        return torch.empty_like(q)
+    _need(out, "out", torch.float16)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    return out
+
+
+def attn_fwd(q, k, v, out=None, *, scale=None, causal=False, cu_seqlens=None,
+             route_bitmask=None, tiles_per_bit=4, stream=None):
+    """Fused attention forward; sizes are read from the tensor shapes.
+
+    dense:  q [B, n_qh, qsl, d], k/v [B, n_kvh, ksl, d]
+    packed: q [n_qh, T, d], k/v [n_kvh, T, d], cu_seqlens int32 [B + 1]
+    route_bitmask: int32 / uint32-valued tensor of packed routing words.
+    Returns out (allocated when None).  Enqueued on torch's current stream.
+    """
+    import torch
+    _need(q, "q", torch.float16)
+    _need(k, "k", torch.float16)
+    _need(v, "v", torch.float16)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, qsl, ksl, d, n_qh, n_kvh = _shapes(q, k, cu_seqlens)
+    out = _out_route(q, out, route_bitmask)
     if scale is None:
         scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     attn_fwd_stream(q, k, v, out, B, qsl, ksl, d, n_qh, n_kvh, scale, causal, cu_seqlens,
@@ -163,3 +181,50 @@ def attn_debug_route_dump(route_bitmask, qsl, ksl, causal, tiles_per_bit, device
     _check(load().attn_debug_route_dump(_ptr(route_bitmask), qsl, ksl, int(bool(causal)),
                                         int(tiles_per_bit), _ptr(out), _stream(stream)))
     return out
+
+
+def attn_fwd_kv8_stream(q, k8, k_scale, v8, v_scale, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal,
+                        cu_seqlens=None, route_bitmask=None, tiles_per_bit=4, stream=None):
+    """Direct mirror of the C entry point (sizes passed explicitly)."""
+    _check(load().attn_fwd_kv8_stream(_ptr(q), _ptr(k8), _ptr(k_scale), _ptr(v8), _ptr(v_scale), _ptr(out),
+                                      B, qsl, ksl, hdim, n_qh, n_kvh, float(scale), int(bool(causal)),
+                                      _ptr(cu_seqlens), _ptr(route_bitmask), int(tiles_per_bit),
+                                      _stream(stream)))
+
+
+def attn_fwd_kv8(q, k8, k_scale, v8, v_scale, out=None, *, scale=None, causal=False, cu_seqlens=None,
+                 route_bitmask=None, tiles_per_bit=4, stream=None):
+    """Fused attention forward on an INT8 key/value cache.
+
+    k8/v8: int8 codes in the layout of k/v; k_scale/v_scale: float32 per row
+    ([B, n_kvh, ksl] dense, [n_kvh, T] packed); the keys and values are
+    k_scale * k8 and v_scale * v8 (attn_quantize_rows makes such a cache).
+    """
+    import torch
+    _need(q, "q", torch.float16)
+    _need(k8, "k8", torch.int8)
+    _need(v8, "v8", torch.int8)
+    _need(k_scale, "k_scale", torch.float32)
+    _need(v_scale, "v_scale", torch.float32)
+    if k8.shape != v8.shape or k_scale.shape != v_scale.shape or tuple(k_scale.shape) != tuple(k8.shape[:-1]):
+        raise ValueError("k8/v8 must share a shape and k_scale/v_scale must be its leading dims")
+    B, qsl, ksl, d, n_qh, n_kvh = _shapes(q, k8, cu_seqlens)
+    out = _out_route(q, out, route_bitmask)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    attn_fwd_kv8_stream(q, k8, k_scale, v8, v_scale, out, B, qsl, ksl, d, n_qh, n_kvh, scale, causal,
+                        cu_seqlens, route_bitmask, tiles_per_bit, stream)
+    return out
+
+
+def attn_quantize_rows(x, stream=None):
+    """(codes int8, scales float32 [leading dims]) of every last-axis row of an
+    fp16 tensor: the INT8 key/value cache encoding, on the device."""
+    import torch
+    _need(x, "x", torch.float16)
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    q8 = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    s = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(load().attn_quantize_rows(_ptr(x), rows, d, _ptr(q8), _ptr(s), _stream(stream)))
+    return q8, s

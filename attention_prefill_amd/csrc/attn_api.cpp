@@ -36,8 +36,13 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 // Checks every argument rule of include/attn.h; touches no device memory.
 attn_status validate(const attn::Problem& p) {
-    if (!p.q || !p.k || !p.v || !p.out)
+    const bool kv8 = p.k8 != nullptr || p.v8 != nullptr || p.k_scale != nullptr || p.v_scale != nullptr;
+    if (kv8) {
+        if (!p.q || !p.k8 || !p.k_scale || !p.v8 || !p.v_scale || !p.out)
+            return fail(ATTN_ERR_NULL, "q, k8, k_scale, v8, v_scale and out must be non-null device pointers");
+    } else if (!p.q || !p.k || !p.v || !p.out) {
         return fail(ATTN_ERR_NULL, "q, k, v and out must be non-null device pointers");
+    }
     if (p.B <= 0 || p.qsl <= 0 || p.ksl <= 0 || p.n_qh <= 0 || p.n_kvh <= 0)
         return fail(ATTN_ERR_SHAPE, "B, qsl, ksl, n_qh, n_kvh must be positive (got %d, %d, %d, %d, %d)",
                     p.B, p.qsl, p.ksl, p.n_qh, p.n_kvh);
@@ -54,13 +59,22 @@ attn_status validate(const attn::Problem& p) {
         return fail(ATTN_ERR_ARG, "scale must be finite and non-zero");
     if (p.route && p.tiles_per_bit < 1)
         return fail(ATTN_ERR_ARG, "tiles_per_bit must be >= 1 with a bitmask (got %d)", p.tiles_per_bit);
-    if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.out))
+    if (kv8) {
+        if (!aligned16(p.q) || !aligned16(p.k8) || !aligned16(p.v8) || !aligned16(p.out))
+            return fail(ATTN_ERR_ARG, "q, k8, v8 and out must be 16-byte aligned");
+        if (!aligned4(p.k_scale) || !aligned4(p.v_scale))
+            return fail(ATTN_ERR_ARG, "k_scale and v_scale must be 4-byte aligned");
+    } else if (!aligned16(p.q) || !aligned16(p.k) || !aligned16(p.v) || !aligned16(p.out)) {
         return fail(ATTN_ERR_ARG, "q, k, v and out must be 16-byte aligned");
+    }
     if ((p.cu_seqlens && !aligned4(p.cu_seqlens)) || (p.route && !aligned4(p.route)))
         return fail(ATTN_ERR_ARG, "cu_seqlens and route_bitmask must be 4-byte aligned");
     const double elems_q = (double)p.B * p.n_qh * p.qsl * p.hdim;
     const double elems_k = (double)p.B * p.n_kvh * p.ksl * p.hdim;
-    if (elems_q > 9.0e15 || elems_k > 9.0e15 || (double)p.B * p.n_kvh * p.ksl > 2.0e9)
+    // the tile loads address one (sequence, kv head) slab of K or V through a
+    // 32-bit buffer range
+    if (elems_q > 9.0e15 || elems_k > 9.0e15 || (double)p.B * p.n_kvh * p.ksl > 2.0e9 ||
+        (double)p.ksl * p.hdim * 2 > 2.0e9)
         return fail(ATTN_ERR_SHAPE, "problem too large");
     return ATTN_OK;
 }
@@ -100,6 +114,19 @@ attn_status run_forward(const attn::Problem& p, hipStream_t st) {
     return ATTN_OK;
 }
 
+attn_status quantize_rows(const void* x, long long rows, int32_t hdim, int8_t* q8, float* scale_out,
+                          int32_t path, hipStream_t st) {
+    if (!x || !q8 || !scale_out) return fail(ATTN_ERR_NULL, "null pointer");
+    if (rows < 0 || rows > 0x7fffffffLL) return fail(ATTN_ERR_SHAPE, "rows must be in [0, 2^31)");
+    if (hdim != 64 && hdim != 128) return fail(ATTN_ERR_UNSUPPORTED, "hdim must be 64 or 128");
+    if (!aligned16(x) || !aligned16(q8) || !aligned4(scale_out))
+        return fail(ATTN_ERR_ARG, "x and q8 must be 16-byte aligned, scale_out 4-byte aligned");
+    hipError_t e = attn::launch_quantize_rows(x, rows, hdim, q8, scale_out, path, st);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,18 +152,39 @@ const char* attn_last_error(void) { return g_last_error.c_str(); }
 
 int32_t attn_abi_version(void) { return ATTN_ABI_VERSION; }
 
+attn_status attn_fwd_kv8_stream(const void* q, const int8_t* k8, const float* k_scale, const int8_t* v8,
+                                const float* v_scale, void* out, int32_t B, int32_t qsl, int32_t ksl,
+                                int32_t hdim, int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                                const int32_t* cu_seqlens, const uint32_t* route_bitmask,
+                                int32_t tiles_per_bit, void* hip_stream) {
+    attn::Problem p{q, nullptr, nullptr, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal != 0,
+                    cu_seqlens, route_bitmask, tiles_per_bit};
+    p.k8 = k8;
+    p.k_scale = k_scale;
+    p.v8 = v8;
+    p.v_scale = v_scale;
+    if (!k8 || !k_scale || !v8 || !v_scale || !q || !out)
+        return fail(ATTN_ERR_NULL, "q, k8, k_scale, v8, v_scale and out must be non-null device pointers");
+    return run_forward(p, (hipStream_t)hip_stream);
+}
+
+attn_status attn_fwd_kv8(const void* q, const int8_t* k8, const float* k_scale, const int8_t* v8,
+                         const float* v_scale, void* out, int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
+                         int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                         const int32_t* cu_seqlens, const uint32_t* route_bitmask, int32_t tiles_per_bit) {
+    return attn_fwd_kv8_stream(q, k8, k_scale, v8, v_scale, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal,
+                               cu_seqlens, route_bitmask, tiles_per_bit, nullptr);
+}
+
+attn_status attn_quantize_rows(const void* x_f16, int64_t rows, int32_t hdim, int8_t* q8, float* scale_out,
+                               void* hip_stream) {
+    return quantize_rows(x_f16, (long long)rows, hdim, q8, scale_out, 0, (hipStream_t)hip_stream);
+}
+
 attn_status attn_debug_quantize_rows(const void* x_f16, int32_t rows, int32_t hdim, int8_t* q8,
                                      float* scale_out, int32_t path, void* hip_stream) {
-    if (!x_f16 || !q8 || !scale_out) return fail(ATTN_ERR_NULL, "null pointer");
-    if (rows < 0) return fail(ATTN_ERR_SHAPE, "rows must be >= 0");
-    if (hdim != 64 && hdim != 128) return fail(ATTN_ERR_UNSUPPORTED, "hdim must be 64 or 128");
     if (path != 0 && path != 1) return fail(ATTN_ERR_ARG, "path must be 0 or 1");
-    if (!aligned16(x_f16) || !aligned16(q8) || !aligned4(scale_out))
-        return fail(ATTN_ERR_ARG, "x and q8 must be 16-byte aligned, scale_out 4-byte aligned");
-    hipError_t e = attn::launch_quantize_rows(x_f16, rows, hdim, q8, scale_out, path, (hipStream_t)hip_stream);
-    if (e != hipSuccess) return hip_fail(e, "quantize launch");
-    g_last_error.clear();
-    return ATTN_OK;
+    return quantize_rows(x_f16, (long long)rows, hdim, q8, scale_out, path, (hipStream_t)hip_stream);
 }
 
 attn_status attn_debug_route_dump(const uint32_t* route_bitmask, int32_t qsl, int32_t ksl,

@@ -19,6 +19,11 @@ struct Problem {
     const int32_t* cu_seqlens;      // device, or nullptr
     const uint32_t* route;          // device, or nullptr
     int tiles_per_bit;
+    // INT8 key/value cache (k and v unused when k8 is set): codes and per-row scales
+    const int8_t* k8 = nullptr;
+    const float* k_scale = nullptr;
+    const int8_t* v8 = nullptr;
+    const float* v_scale = nullptr;
 };
 
 // Device scratch a forward call needs (bytes): quantised K rows for routed
@@ -30,7 +35,7 @@ size_t forward_scratch_bytes(const Problem& p);
 hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t stream);
 
 // Test hooks (include/attn.h).
-hipError_t launch_quantize_rows(const void* x, int rows, int hdim, int8_t* q8, float* s,
+hipError_t launch_quantize_rows(const void* x, long long rows, int hdim, int8_t* q8, float* s,
                                 int path, hipStream_t stream);
 hipError_t launch_route_dump(const uint32_t* route, int qsl, int ksl, bool causal,
                              int tiles_per_bit, uint8_t* out, hipStream_t stream);

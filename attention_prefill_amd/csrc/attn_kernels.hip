@@ -54,6 +54,7 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -145,6 +146,17 @@ __device__ __forceinline__ void quantize_q_regs(const f16x8 (&qf)[HD / 16], i32x
     s_out = s;
 }
 
+// Exact int8 -> fp16 of the four signed bytes of w: with u = b + 128 in the low
+// byte and 0x64 above it, a 16-bit lane holds the fp16 value 1024 + u, and
+// subtracting 1152 leaves b.  Lanes hold bytes 0,1 (first word), 2,3 (second).
+__device__ __forceinline__ u32x2 widen_i8x4(unsigned w) {
+    const unsigned u = w ^ 0x80808080u;
+    const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + bias;
+    const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + bias;
+    return u32x2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)};
+}
+
 // ---------------------------------------------------------------------------
 // Routing decode: bit of group kt / tiles_per_bit in the row of query tile qt.
 // ---------------------------------------------------------------------------
@@ -154,11 +166,12 @@ __device__ __forceinline__ bool route_bit(const uint32_t* row, int kt, int tiles
 }
 
 // ---------------------------------------------------------------------------
-// LDS layout of one stage: the K tile (fp16 [key][d], or INT8 codes [key][d]
-// followed by the 64 scaled K scales) and the V tile stored transposed,
-// [d][key], so that the P.V operand (8 consecutive keys of one d) is a single
-// 16-byte read.  Row pitches are padded so that the row-parallel operand
-// reads and the staging writes spread over the banks.
+// LDS layout of one stage: the K tile (fp16 [key][d], or INT8 codes
+// [key][d]), the V tile stored transposed, [d][key], so that the P.V operand
+// (8 consecutive keys of one d) is a single 16-byte read, and the tile's
+// per-key scales (K scales times |scale|*log2(e), then V scales; INT8 tiles
+// and INT8 key/value caches).  Row pitches are padded so that the
+// row-parallel operand reads and the staging writes spread over the banks.
 // ---------------------------------------------------------------------------
 template <int HD>
 struct Lds {
@@ -166,10 +179,11 @@ struct Lds {
     static constexpr int VTP = BN + 8;           // fp16 elements per V^T row
     static constexpr int K8P = HD + 16;          // bytes per INT8 K row
     static constexpr int KBYTES = BN * KP * 2;
-    static constexpr int K8BYTES = BN * K8P + BN * 4;
+    static constexpr int K8BYTES = BN * K8P;
     static constexpr int KREG = KBYTES > K8BYTES ? KBYTES : K8BYTES;
     static constexpr int VBYTES = HD * VTP * 2;
-    static constexpr int STAGE = KREG + VBYTES;
+    static constexpr int SCL = 2 * BN * 4;
+    static constexpr int STAGE = KREG + VBYTES + SCL;
     static constexpr int TOTAL = 2 * STAGE;
 };
 
@@ -178,8 +192,10 @@ struct FwdArgs {
     const _Float16* k;
     const _Float16* v;
     _Float16* out;
-    const int8_t* k8;       // quantised K rows (routed), same row order as k
+    const int8_t* k8;       // INT8 K rows (routed: quantised per call; cache: the caller's)
     const float* sk;        // their scales
+    const int8_t* v8;       // INT8 V rows of a key/value cache, or null
+    const float* sv;        // their scales
     const int32_t* cu;      // packed sequence offsets, or null
     const uint32_t* route;  // routing bitmask, or null
     int B, qsl, ksl, n_qh, n_kvh, G, HPW;
@@ -205,7 +221,7 @@ constexpr float TAU = 8.0f;
 // ---------------------------------------------------------------------------
 // Fused forward kernel.
 // ---------------------------------------------------------------------------
-template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED>
+template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8>
 __global__ __launch_bounds__(NW * KS * 64, (NW == 2 || KS > 1) ? 1 : (BN == 32 ? 3 : 2))
 void attn_fwd_kernel(FwdArgs a) {
     using L = Lds<HD>;
@@ -219,7 +235,7 @@ void attn_fwd_kernel(FwdArgs a) {
     constexpr int NDB = HD / 32;                       // 32-row blocks of d in O^T
     // Tiles in flight ahead of the one computed.  Two need a second staging
     // set, which only the hdim-64 FP16 kernel has registers for.
-    constexpr int PF = (HD == 64 && !ROUTED && NW == 4 && BN == 64) ? 2 : 1;
+    constexpr int PF = (HD == 64 && !ROUTED && !KV8 && NW == 4 && BN == 64) ? 2 : 1;
     // Request all of a tile's K and V fragments before its first MFMA (the
     // hdim-64 kernel has the registers for them).
     constexpr bool EARLY = (HD == 64);
@@ -282,8 +298,10 @@ void attn_fwd_kernel(FwdArgs a) {
     _Float16* ob = a.out + qrow0 * HD;
     const _Float16* kb = a.k + krow0 * HD;
     const _Float16* vb = a.v + krow0 * HD;
-    const int8_t* k8b = ROUTED ? a.k8 + krow0 * HD : nullptr;
-    const float* skb = ROUTED ? a.sk + krow0 : nullptr;
+    const int8_t* k8b = (ROUTED || KV8) ? a.k8 + krow0 * HD : nullptr;
+    const float* skb = (ROUTED || KV8) ? a.sk + krow0 : nullptr;
+    const int8_t* v8b = KV8 ? a.v8 + krow0 * HD : nullptr;
+    const float* svb = KV8 ? a.sv + krow0 : nullptr;
 
     const int off = CAUSAL ? (Lk - Lq) : 0;     // bottom-right alignment
     const int m0 = mb * BM;
@@ -328,10 +346,14 @@ void attn_fwd_kernel(FwdArgs a) {
     const int slab = Lk * HD * 2;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, slab, BUF_DWORD3);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, slab, BUF_DWORD3);
-    __amdgpu_buffer_rsrc_t k8rs = krs, skrs = krs;
-    if constexpr (ROUTED) {
+    __amdgpu_buffer_rsrc_t k8rs = krs, skrs = krs, v8rs = krs, svrs = krs;
+    if constexpr (ROUTED || KV8) {
         k8rs = __builtin_amdgcn_make_buffer_rsrc((void*)k8b, (short)0, Lk * HD, BUF_DWORD3);
         skrs = __builtin_amdgcn_make_buffer_rsrc((void*)skb, (short)0, Lk * 4, BUF_DWORD3);
+    }
+    if constexpr (KV8) {
+        v8rs = __builtin_amdgcn_make_buffer_rsrc((void*)v8b, (short)0, Lk * HD, BUF_DWORD3);
+        svrs = __builtin_amdgcn_make_buffer_rsrc((void*)svb, (short)0, Lk * 4, BUF_DWORD3);
     }
     // Staging registers of one tile between its global loads and its LDS
     // store.  With PF = 2 two sets alternate, so the loads of tile t+2 are
@@ -339,7 +361,9 @@ void attn_fwd_kernel(FwdArgs a) {
     struct Staging {
         u32x4 kreg[KCH];
         u32x4 vreg[VB][4];
+        u32x2 v8reg[VB][4];     // INT8 V cache: 8 codes of each of 4 keys
         u32x4 skreg;
+        u32x4 svreg;
     };
     // The two-set pipeline waits for the older set with a load count, so every
     // lane issues the same number of loads: the first half of the waves loads
@@ -399,7 +423,7 @@ void attn_fwd_kernel(FwdArgs a) {
         u32x4(&kreg)[KCH] = sg.kreg;
         u32x4(&vreg)[VB][4] = sg.vreg;
         u32x4& skreg = sg.skreg;
-        if (ROUTED && i8) {
+        if (KV8 || (ROUTED && i8)) {
             const int soff = kt * BN * HD;
 #pragma unroll
             for (int n = 0; n < K8CH; ++n) {
@@ -418,17 +442,36 @@ void attn_fwd_kernel(FwdArgs a) {
                     kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, c * 16, soff, 0));
             }
         }
-        const int soff = kt * BN * HD * 2;
+        if constexpr (KV8) {
+            const int soff = kt * BN * HD;
 #pragma unroll
-        for (int n = 0; n < VB; ++n) {
-            const int bi = tid + n * NT;
-            if (VBLK % NT == 0 || bi < VBLK) {
-                const int kg = bi % (BN / 4);
-                const int dc = bi / (BN / 4);
+            for (int n = 0; n < VB; ++n) {
+                const int bi = tid + n * NT;
+                if (VBLK % NT == 0 || bi < VBLK) {
+                    const int kg = bi % (BN / 4);
+                    const int dc = bi / (BN / 4);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    vreg[n][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        vrs, ((4 * kg + i) * HD + 8 * dc) * 2, soff, 0));
+                    for (int i = 0; i < 4; ++i)
+                        sg.v8reg[n][i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                            v8rs, (4 * kg + i) * HD + 8 * dc, soff, 0));
+                }
+            }
+            if (tid >= BN / 4 && tid < BN / 2)
+                sg.svreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    svrs, (tid - BN / 4) * 16, kt * BN * 4, 0));
+        } else {
+            const int soff = kt * BN * HD * 2;
+#pragma unroll
+            for (int n = 0; n < VB; ++n) {
+                const int bi = tid + n * NT;
+                if (VBLK % NT == 0 || bi < VBLK) {
+                    const int kg = bi % (BN / 4);
+                    const int dc = bi / (BN / 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        vreg[n][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                            vrs, ((4 * kg + i) * HD + 8 * dc) * 2, soff, 0));
+                }
             }
         }
     };
@@ -439,6 +482,9 @@ void attn_fwd_kernel(FwdArgs a) {
         const u32x4& skreg = sg.skreg;
         char* kbuf = smem + (stage * KS + kgp) * L::STAGE;
         _Float16* vt = (_Float16*)(kbuf + L::KREG);
+        float* scl = (float*)(kbuf + L::KREG + L::VBYTES);
+        if ((KV8 || (ROUTED && i8)) && tid < BN / 4)
+            *(f32x4*)(scl + 4 * tid) = __builtin_bit_cast(f32x4, skreg) * a.c;
         if (ROUTED && i8) {
 #pragma unroll
             for (int n = 0; n < K8CH; ++n) {
@@ -447,10 +493,20 @@ void attn_fwd_kernel(FwdArgs a) {
                 const int col = (c % (HD / 16)) * 16;
                 if (K8TOT % NT == 0 || c < K8TOT) *(u32x4*)(kbuf + row * L::K8P + col) = kreg[n];
             }
-            if (tid < BN / 4) {
-                float* skc = (float*)(kbuf + BN * L::K8P);
-                const f32x4 sv = __builtin_bit_cast(f32x4, skreg);
-                *(f32x4*)(skc + 4 * tid) = sv * a.c;
+        } else if (KV8) {
+            // FP16 route on an INT8 key cache: the codes widened to fp16 (exact)
+            _Float16* k16 = (_Float16*)kbuf;
+#pragma unroll
+            for (int n = 0; n < K8CH; ++n) {
+                const int c = tid + n * NT;
+                const int row = c / (HD / 16);
+                const int col = (c % (HD / 16)) * 16;
+                if (K8TOT % NT == 0 || c < K8TOT) {
+                    const u32x2 w0 = widen_i8x4(kreg[n][0]), w1 = widen_i8x4(kreg[n][1]);
+                    const u32x2 w2 = widen_i8x4(kreg[n][2]), w3 = widen_i8x4(kreg[n][3]);
+                    *(u32x4*)(k16 + row * L::KP + col) = u32x4{w0[0], w0[1], w1[0], w1[1]};
+                    *(u32x4*)(k16 + row * L::KP + col + 8) = u32x4{w2[0], w2[1], w3[0], w3[1]};
+                }
             }
         } else {
             _Float16* k16 = (_Float16*)kbuf;
@@ -468,7 +524,18 @@ void attn_fwd_kernel(FwdArgs a) {
             if (VBLK % NT == 0 || bi < VBLK) {
                 const int kg = bi % (BN / 4);
                 const int dc = bi / (BN / 4);
-                const u32x4 r0w = vreg[n][0], r1w = vreg[n][1], r2w = vreg[n][2], r3w = vreg[n][3];
+                u32x4 r0w = vreg[n][0], r1w = vreg[n][1], r2w = vreg[n][2], r3w = vreg[n][3];
+                if constexpr (KV8) {
+                    // INT8 value cache: rows of 8 codes widened to 8 fp16 values
+                    auto row8 = [](u32x2 c) __attribute__((always_inline)) {
+                        const u32x2 a0 = widen_i8x4(c[0]), a1 = widen_i8x4(c[1]);
+                        return u32x4{a0[0], a0[1], a1[0], a1[1]};
+                    };
+                    r0w = row8(sg.v8reg[n][0]);
+                    r1w = row8(sg.v8reg[n][1]);
+                    r2w = row8(sg.v8reg[n][2]);
+                    r3w = row8(sg.v8reg[n][3]);
+                }
                 _Float16* dst = vt + (8 * dc) * L::VTP + 4 * kg;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -482,6 +549,8 @@ void attn_fwd_kernel(FwdArgs a) {
                 }
             }
         }
+        if (KV8 && tid >= BN / 4 && tid < BN / 2)
+            *(f32x4*)(scl + BN + 4 * (tid - BN / 4)) = __builtin_bit_cast(f32x4, sg.svreg);
     };
 
     // ---- state --------------------------------------------------------------------
@@ -502,8 +571,26 @@ void attn_fwd_kernel(FwdArgs a) {
         float x[NKB][16];
         float amul;
         f16x8 vfr[EARLY ? 2 * NKB : 1][EARLY ? NDB : 1];   // V fragments requested with K
+        // per-key scales of the tile (INT8 tiles, key/value caches)
+        const float* skc = (const float*)(kbuf + L::KREG + L::VBYTES);
+        const float* svc = skc + BN;
+        // x[kb32][i] *= the scale of its key: this lane's keys are
+        // 32*kb32 + 8*g + (i%8) + 16*(i/8)
+        auto key_scale = [&](int kb32) __attribute__((always_inline)) {
+            const float* sp = skc + 32 * kb32 + 8 * g;
+            const f32x4 s0 = *(const f32x4*)(sp);
+            const f32x4 s1 = *(const f32x4*)(sp + 4);
+            const f32x4 s2 = *(const f32x4*)(sp + 16);
+            const f32x4 s3 = *(const f32x4*)(sp + 20);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[kb32][i] *= s0[i];
+                x[kb32][4 + i] *= s1[i];
+                x[kb32][8 + i] *= s2[i];
+                x[kb32][12 + i] *= s3[i];
+            }
+        };
         if (ROUTED && i8) {
-            const float* skc = (const float*)(kbuf + BN * L::K8P);
 #pragma unroll
             for (int kb32 = 0; kb32 < NKB; ++kb32) {
                 i32x16 acc = i32x16{};
@@ -513,19 +600,9 @@ void attn_fwd_kernel(FwdArgs a) {
                     i32x4 av = *(const i32x4*)(kr + 32 * ks);
                     acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, q8[ks], acc, 0, 0, 0);
                 }
-                // this lane's keys: 32*kb32 + 8*g + (i%8) + 16*(i/8)
-                const float* sp = skc + 32 * kb32 + 8 * g;
-                const f32x4 s0 = *(const f32x4*)(sp);
-                const f32x4 s1 = *(const f32x4*)(sp + 4);
-                const f32x4 s2 = *(const f32x4*)(sp + 16);
-                const f32x4 s3 = *(const f32x4*)(sp + 20);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[kb32][i] = (float)acc[i] * s0[i];
-                    x[kb32][4 + i] = (float)acc[4 + i] * s1[i];
-                    x[kb32][8 + i] = (float)acc[8 + i] * s2[i];
-                    x[kb32][12 + i] = (float)acc[12 + i] * s3[i];
-                }
+                for (int i = 0; i < 16; ++i) x[kb32][i] = (float)acc[i];
+                key_scale(kb32);
             }
             amul = sq_mul;
         } else {
@@ -572,6 +649,12 @@ void attn_fwd_kernel(FwdArgs a) {
                 }
             }
             amul = a.c;
+            if constexpr (KV8) {
+                // scores against the widened codes, times s_k * |scale| * log2(e)
+#pragma unroll
+                for (int kb32 = 0; kb32 < NKB; ++kb32) key_scale(kb32);
+                amul = 1.0f;
+            }
         }
 
         if constexpr (MASK) {
@@ -621,11 +704,18 @@ void attn_fwd_kernel(FwdArgs a) {
         for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
+                // value-cache scales of keys 32*kb32 + 8*g + 16*t + j: the P that
+                // multiplies the widened V codes is p * s_v (the sum keeps p)
+                f32x4 v0 = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, v1 = v0;
+                if constexpr (KV8) {
+                    v0 = *(const f32x4*)(svc + 32 * kb32 + 8 * g + 16 * t);
+                    v1 = *(const f32x4*)(svc + 32 * kb32 + 8 * g + 16 * t + 4);
+                }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb32][8 * t + j], amul, nm));
                     rs += p;
-                    pk[kb32][t][j] = (_Float16)p;
+                    pk[kb32][t][j] = (_Float16)(KV8 ? p * (j < 4 ? v0[j] : v1[j - 4]) : p);
                 }
             }
         l_run += rs;
@@ -914,9 +1004,9 @@ hipError_t set_lds(K kernel, int bytes) {
     return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED>
+template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8>
 hipError_t launch_fwd_t(const FwdArgs& a, int grid, hipStream_t st) {
-    auto kern = attn_fwd_kernel<HD, NW, KS, CAUSAL, VARLEN, ROUTED>;
+    auto kern = attn_fwd_kernel<HD, NW, KS, CAUSAL, VARLEN, ROUTED, KV8>;
     constexpr int lds = Lds<HD>::TOTAL * KS;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
@@ -924,34 +1014,42 @@ hipError_t launch_fwd_t(const FwdArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int HD, int NW, int KS>
-hipError_t dispatch_flags(const FwdArgs& a, int grid, bool causal, bool varlen, bool routed,
-                          hipStream_t st) {
-    if (routed) {
-        if constexpr (KS == 1) {
-            if (varlen)
-                return causal ? launch_fwd_t<HD, NW, KS, true, true, true>(a, grid, st)
-                              : launch_fwd_t<HD, NW, KS, false, true, true>(a, grid, st);
-            return causal ? launch_fwd_t<HD, NW, KS, true, false, true>(a, grid, st)
-                          : launch_fwd_t<HD, NW, KS, false, false, true>(a, grid, st);
-        }
-        return hipErrorInvalidConfiguration;   // routed calls use one key group
+template <int HD, int NW, int KS, bool ROUTED, bool KV8>
+hipError_t dispatch_mask(const FwdArgs& a, int grid, bool causal, bool varlen, hipStream_t st) {
+    if (varlen)
+        return causal ? launch_fwd_t<HD, NW, KS, true, true, ROUTED, KV8>(a, grid, st)
+                      : launch_fwd_t<HD, NW, KS, false, true, ROUTED, KV8>(a, grid, st);
+    return causal ? launch_fwd_t<HD, NW, KS, true, false, ROUTED, KV8>(a, grid, st)
+                  : launch_fwd_t<HD, NW, KS, false, false, ROUTED, KV8>(a, grid, st);
+}
+
+// Instantiated shapes: two-wave workgroups for routed calls with an odd head
+// group only, two key groups for non-routed FP16 calls only.
+template <int HD>
+hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, bool varlen, bool routed,
+                    bool kv8, hipStream_t st) {
+    if (NW == 2) {
+        if (!routed || KS != 1) return hipErrorInvalidConfiguration;
+        return kv8 ? dispatch_mask<HD, 2, 1, true, true>(a, grid, causal, varlen, st)
+                   : dispatch_mask<HD, 2, 1, true, false>(a, grid, causal, varlen, st);
     }
-    if constexpr (NW == 4) {
-        if (varlen)
-            return causal ? launch_fwd_t<HD, NW, KS, true, true, false>(a, grid, st)
-                          : launch_fwd_t<HD, NW, KS, false, true, false>(a, grid, st);
-        return causal ? launch_fwd_t<HD, NW, KS, true, false, false>(a, grid, st)
-                      : launch_fwd_t<HD, NW, KS, false, false, false>(a, grid, st);
+    if (KS == 2) {
+        if (routed || kv8) return hipErrorInvalidConfiguration;
+        return dispatch_mask<HD, 4, 2, false, false>(a, grid, causal, varlen, st);
     }
-    return hipErrorInvalidConfiguration;   // two-wave workgroups exist for routed calls only
+    if (routed)
+        return kv8 ? dispatch_mask<HD, 4, 1, true, true>(a, grid, causal, varlen, st)
+                   : dispatch_mask<HD, 4, 1, true, false>(a, grid, causal, varlen, st);
+    return kv8 ? dispatch_mask<HD, 4, 1, false, true>(a, grid, causal, varlen, st)
+               : dispatch_mask<HD, 4, 1, false, false>(a, grid, causal, varlen, st);
 }
 
 }  // namespace
 
-hipError_t launch_quantize_rows(const void* x, int rows, int hdim, int8_t* q8, float* s,
+hipError_t launch_quantize_rows(const void* x, long long rows, int hdim, int8_t* q8, float* s,
                                 int path, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
+    if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
     if (path == 0) {
         const long long threads = (long long)rows * (hdim / 8);
         const int grid = (int)((threads + 255) / 256);
@@ -962,13 +1060,13 @@ hipError_t launch_quantize_rows(const void* x, int rows, int hdim, int8_t* q8, f
             hipLaunchKernelGGL(quantize_rows_kernel<128>, dim3(grid), dim3(256), 0, st,
                                (const _Float16*)x, q8, s, (long long)rows);
     } else {
-        const int grid = (rows + 31) / 32;
+        const int grid = (int)((rows + 31) / 32);
         if (hdim == 64)
             hipLaunchKernelGGL(quantize_qrows_kernel<64>, dim3(grid), dim3(64), 0, st,
-                               (const _Float16*)x, q8, s, rows);
+                               (const _Float16*)x, q8, s, (int)rows);
         else
             hipLaunchKernelGGL(quantize_qrows_kernel<128>, dim3(grid), dim3(64), 0, st,
-                               (const _Float16*)x, q8, s, rows);
+                               (const _Float16*)x, q8, s, (int)rows);
     }
     return hipGetLastError();
 }
@@ -1019,6 +1117,7 @@ static Plan make_plan(const Problem& p) {
     Plan pl{};
     const bool varlen = p.cu_seqlens != nullptr;
     const bool routed = p.route != nullptr;
+    const bool kv8 = p.k8 != nullptr;
     const int G = p.n_qh / p.n_kvh;
     // workgroup shape: a routed workgroup stays inside one 64-row query tile
     pl.NW = 4;
@@ -1037,9 +1136,10 @@ static Plan make_plan(const Problem& p) {
     const long long waves = (long long)pl.combos * pl.n_mblk * pl.NW;
     const long long simds = 4LL * cu_count();
     const int n_kt = (p.ksl + BN - 1) / BN;
-    pl.KS = (!routed && pl.NW == 4 && waves < 2 * simds && n_kt >= 2) ? 2 : 1;
+    const bool kg2_ok = !routed && !kv8 && pl.NW == 4;
+    pl.KS = (kg2_ok && waves < 2 * simds && n_kt >= 2) ? 2 : 1;
     const char* force_kg = getenv("ATTN_KEY_GROUPS");
-    if (!routed && pl.NW == 4 && force_kg && (force_kg[0] == '1' || force_kg[0] == '2') && force_kg[1] == 0)
+    if (kg2_ok && force_kg && (force_kg[0] == '1' || force_kg[0] == '2') && force_kg[1] == 0)
         pl.KS = force_kg[0] - '0';
     int ks = 1;
     while (ks < 8 && waves * pl.KS * ks < 2 * simds && n_kt >= 16 * ks) ks *= 2;
@@ -1049,7 +1149,7 @@ static Plan make_plan(const Problem& p) {
     pl.grid = (long long)pl.combos * pl.ksplit * pl.n_mblk;
     pl.out_rows = varlen ? (long long)p.n_qh * p.qsl : (long long)p.B * p.n_qh * p.qsl;
     size_t off = 0;
-    if (routed) {
+    if (routed && !kv8) {
         const size_t krows = varlen ? (size_t)p.n_kvh * p.ksl : (size_t)p.B * p.n_kvh * p.ksl;
         pl.k8_off = off;
         off += round_up(krows * p.hdim);
@@ -1086,8 +1186,10 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
     a.c = fabsf(p.scale) * LOG2E;
     a.neg = p.scale < 0.0f ? 1 : 0;
     a.tiles_per_bit = p.route ? p.tiles_per_bit : 1;
-    a.k8 = nullptr;
-    a.sk = nullptr;
+    a.k8 = p.k8;            // INT8 key/value cache, or null
+    a.sk = p.k_scale;
+    a.v8 = p.v8;
+    a.sv = p.v_scale;
     a.HPW = pl.HPW;
     a.combos = pl.combos;
     a.n_mblk = pl.n_mblk;
@@ -1098,15 +1200,19 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
     const bool varlen = p.cu_seqlens != nullptr;
     const bool routed = p.route != nullptr;
 
+    const bool kv8 = p.k8 != nullptr;
     if (routed) {
         const int n_kt = (p.ksl + TK - 1) / TK;
         const int n_g = (n_kt + p.tiles_per_bit - 1) / p.tiles_per_bit;
         a.wpr = (n_g + 31) / 32;
-        const size_t krows = varlen ? (size_t)p.n_kvh * p.ksl : (size_t)p.B * p.n_kvh * p.ksl;
-        a.k8 = (const int8_t*)((char*)scratch + pl.k8_off);
-        a.sk = (const float*)((char*)scratch + pl.sk_off);
-        hipError_t e = launch_quantize_rows(p.k, (int)krows, p.hdim, (int8_t*)a.k8, (float*)a.sk, 0, st);
-        if (e != hipSuccess) return e;
+        if (!kv8) {
+            // INT8 codes of every K row, once per call (a cache brings its own)
+            const size_t krows = varlen ? (size_t)p.n_kvh * p.ksl : (size_t)p.B * p.n_kvh * p.ksl;
+            a.k8 = (const int8_t*)((char*)scratch + pl.k8_off);
+            a.sk = (const float*)((char*)scratch + pl.sk_off);
+            hipError_t e = launch_quantize_rows(p.k, (long long)krows, p.hdim, (int8_t*)a.k8, (float*)a.sk, 0, st);
+            if (e != hipSuccess) return e;
+        }
     } else {
         a.wpr = 0;
     }
@@ -1116,13 +1222,9 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
     const int grid = (int)pl.grid;
     hipError_t e;
     if (p.hdim == 64)
-        e = pl.NW == 2   ? dispatch_flags<64, 2, 1>(a, grid, p.causal, varlen, routed, st)
-            : pl.KS == 1 ? dispatch_flags<64, 4, 1>(a, grid, p.causal, varlen, routed, st)
-                         : dispatch_flags<64, 4, 2>(a, grid, p.causal, varlen, routed, st);
+        e = dispatch<64>(a, grid, pl.NW, pl.KS, p.causal, varlen, routed, kv8, st);
     else
-        e = pl.NW == 2   ? dispatch_flags<128, 2, 1>(a, grid, p.causal, varlen, routed, st)
-            : pl.KS == 1 ? dispatch_flags<128, 4, 1>(a, grid, p.causal, varlen, routed, st)
-                         : dispatch_flags<128, 4, 2>(a, grid, p.causal, varlen, routed, st);
+        e = dispatch<128>(a, grid, pl.NW, pl.KS, p.causal, varlen, routed, kv8, st);
     if (e != hipSuccess || pl.ksplit == 1) return e;
     const long long threads = pl.out_rows * (p.hdim / 8);
     const int mgrid = (int)((threads + 255) / 256);

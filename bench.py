@@ -61,7 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fp16-compare", action="store_true",
                     help="routed workloads: also time the same inputs with an all-FP16 (zero) "
-                         "bitmask and with no bitmask")
+                         "bitmask and with no bitmask; INT8-cache workloads: also time the "
+                         "fp16 K and V the cache was encoded from")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (reference for HBM byte counters) and exit")
     return ap.parse_args()
@@ -83,13 +84,23 @@ class Call:
         self.A = A
         self.metric_flop, self.visited_flop = W.workload_flop(w)
         self.zero_route = None if r is None else torch.zeros_like(self.route)
+        if w.kv8:
+            # the INT8 key/value cache, encoded on the device before timing
+            self.k8, self.sk = A.attn_quantize_rows(self.k)
+            self.v8, self.sv = A.attn_quantize_rows(self.v)
 
-    def __call__(self, stream, route="drawn"):
+    def __call__(self, stream, route="drawn", fp16_kv=False):
         """route: "drawn" (the workload's bitmask), "zero" (same kernel, every
-        tile FP16) or "none" (no bitmask: the dense kernel)."""
+        tile FP16) or "none" (no bitmask: the dense kernel).  fp16_kv: a cache
+        workload's call on the fp16 K and V it was encoded from."""
         w = self.w
         B = len(w.seqlens) if w.varlen else w.B
         rt = {"drawn": self.route, "zero": self.zero_route, "none": None}[route]
+        if w.kv8 and not fp16_kv:
+            self.A.attn_fwd_kv8_stream(self.q, self.k8, self.sk, self.v8, self.sv, self.out, B, w.qsl, w.ksl,
+                                       w.hdim, w.n_qh, w.n_kvh, w.scale, w.causal, self.cu, rt,
+                                       w.tiles_per_bit or 4, stream)
+            return
         self.A.attn_fwd_stream(self.q, self.k, self.v, self.out, B, w.qsl, w.ksl, w.hdim, w.n_qh,
                                w.n_kvh, w.scale, w.causal, self.cu, rt, w.tiles_per_bit or 4, stream)
 
@@ -104,6 +115,9 @@ def cpu_baseline(calls, budget_s=12.0):
     for c in calls:
         w = c.w
         q, k, v = c.host
+        if w.kv8:
+            k8, sk = oracle.quantize_rows(k)
+            v8, sv = oracle.quantize_rows(v)
         G = w.n_qh // w.n_kvh
         cu = W.cu_seqlens_of(w.seqlens) if w.varlen else None
         spent = 0.0
@@ -116,10 +130,18 @@ def cpu_baseline(calls, budget_s=12.0):
                 qs, ks, vs = q[h:h + 1], k[hk:hk + 1], v[hk:hk + 1]
             else:
                 qs, ks, vs = q[:, h:h + 1], k[:, hk:hk + 1], v[:, hk:hk + 1]
+            sl = (slice(hk, hk + 1),) if w.varlen else (slice(None), slice(hk, hk + 1))
             t0 = time.perf_counter()
-            oracle.attn_fwd(np.ascontiguousarray(qs), np.ascontiguousarray(ks), np.ascontiguousarray(vs),
-                            scale=w.scale, causal=w.causal, cu_seqlens=cu, route=c.route_host,
-                            tiles_per_bit=w.tiles_per_bit or 4, nthreads=threads)
+            if w.kv8:
+                oracle.attn_fwd_kv8(np.ascontiguousarray(qs), np.ascontiguousarray(k8[sl]),
+                                    np.ascontiguousarray(sk[sl]), np.ascontiguousarray(v8[sl]),
+                                    np.ascontiguousarray(sv[sl]), scale=w.scale, causal=w.causal,
+                                    cu_seqlens=cu, route=c.route_host, tiles_per_bit=w.tiles_per_bit or 4,
+                                    nthreads=threads)
+            else:
+                oracle.attn_fwd(np.ascontiguousarray(qs), np.ascontiguousarray(ks), np.ascontiguousarray(vs),
+                                scale=w.scale, causal=w.causal, cu_seqlens=cu, route=c.route_host,
+                                tiles_per_bit=w.tiles_per_bit or 4, nthreads=threads)
             spent += time.perf_counter() - t0
             heads += 1
         flop += c.metric_flop * heads / w.n_qh
@@ -209,9 +231,10 @@ def main():
     dc = calls[dom]
     achieved = dc.visited_flop / (dom_ms * 1e-3) / 1e12
     dw = dc.w
-    dom_name = "attn_fwd_kernel hd%d %s%s%s" % (dw.hdim, "causal" if dw.causal else "noncausal",
-                                                 " varlen" if dw.varlen else "",
-                                                 " routed" if dw.tiles_per_bit else "")
+    dom_name = "attn_fwd_kernel hd%d %s%s%s%s" % (dw.hdim, "causal" if dw.causal else "noncausal",
+                                                   " varlen" if dw.varlen else "",
+                                                   " routed" if dw.tiles_per_bit else "",
+                                                   " kv8" if dw.kv8 else "")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP16_PEAK_TFLOPS, 4),
                 "traffic": hbm_traffic(dom_name), "kernel": dom_name,
@@ -222,7 +245,7 @@ def main():
     for c in calls:
         w = c.w
         key = (w.qsl, w.ksl, w.hdim, w.n_qh, w.n_kvh, int(w.causal))
-        if w.B == 1 and not w.varlen and not w.tiles_per_bit and key in PAGE_ROWS:
+        if w.B == 1 and not w.varlen and not w.tiles_per_bit and not w.kv8 and key in PAGE_ROWS:
             page.append(PAGE_ROWS[key][0] / 64.0)
     vs = None
     if len(page) == len(calls):
@@ -232,34 +255,42 @@ def main():
     cfg = {"workload": args.workload, "B": len(w0.seqlens) if w0.varlen else w0.B, "qsl": w0.qsl,
            "ksl": w0.ksl, "hdim": w0.hdim, "n_qh": w0.n_qh, "n_kvh": w0.n_kvh,
            "causal": [c.w.causal for c in calls] if len(calls) > 1 else w0.causal,
-           "seqlens": w0.seqlens, "tiles_per_bit": w0.tiles_per_bit or None,
+           "seqlens": w0.seqlens, "tiles_per_bit": w0.tiles_per_bit or None, "kv_cache_int8": w0.kv8,
            "calls_per_step": len(calls)}
     rec = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": vs, "dtype": "fp16",
-           "data": "synthetic: i.i.d. N(0,1) Q/K/V cast to fp16 (numpy default_rng, seeded)",
+           "data": "synthetic: i.i.d. N(0,1) Q/K/V cast to fp16 (numpy default_rng, seeded)" +
+                   ("; K and V as an INT8 key/value cache encoded on the device"
+                    if any(c.w.kv8 for c in calls) else ""),
            "config": cfg, "pct_fp16_peak": round(100 * value / FP16_PEAK_TFLOPS, 2),
            "roofline": roofline}
+    def time_route(route, fp16_kv=False):
+        for _ in range(args.warmup):
+            for c in calls:
+                c(stream, route, fp16_kv)
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for _ in range(args.steps):
+            for c in calls:
+                c(stream, route, fp16_kv)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - ta) / args.steps
+
     if args.fp16_compare and any(c.route is not None for c in calls):
         # the all-FP16 run of the same inputs: the same kernel with a zero
         # bitmask, and for context the dense kernel with no bitmask at all
-        def time_route(route):
-            for _ in range(args.warmup):
-                for c in calls:
-                    c(stream, route)
-            torch.cuda.synchronize()
-            ta = time.perf_counter()
-            for _ in range(args.steps):
-                for c in calls:
-                    c(stream, route)
-            torch.cuda.synchronize()
-            return (time.perf_counter() - ta) / args.steps
         zero_step = time_route("zero")
         dense_step = time_route("none")
         rec["all_fp16_ms_per_step"] = round(zero_step * 1e3, 5)
         rec["routed_speedup_vs_all_fp16"] = round(zero_step / sec_per_step, 4)
         rec["dense_no_bitmask_ms_per_step"] = round(dense_step * 1e3, 5)
         rec["routed_speedup_vs_dense"] = round(dense_step / sec_per_step, 4)
+    if args.fp16_compare and any(c.w.kv8 for c in calls):
+        # the same call on the fp16 K and V the cache was encoded from
+        kv16_step = time_route("drawn", fp16_kv=True)
+        rec["fp16_kv_ms_per_step"] = round(kv16_step * 1e3, 5)
+        rec["kv8_speedup_vs_fp16_kv"] = round(kv16_step / sec_per_step, 4)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(calls)
     print(json.dumps(rec), flush=True)

@@ -63,7 +63,8 @@ typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,         /* q, k, v or out is NULL */
     ATTN_ERR_SHAPE = 2,        /* a size <= 0, n_qh % n_kvh != 0, causal with
-                                  qsl > ksl, or packed with qsl != ksl */
+                                  qsl > ksl, packed with qsl != ksl, or a
+                                  K / V slab of 2^31 bytes or more */
     ATTN_ERR_UNSUPPORTED = 3,  /* hdim not 64 or 128 */
     ATTN_ERR_ARG = 4,          /* scale not finite or zero; tiles_per_bit < 1
                                   with a bitmask; pointer not 16-byte aligned */
@@ -86,6 +87,47 @@ attn_status attn_fwd_stream(const void* q, const void* k, const void* v, void* o
                             int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
                             const int32_t* cu_seqlens, const uint32_t* route_bitmask,
                             int32_t tiles_per_bit, void* hip_stream);
+
+/* Fused attention forward on an INT8 key/value cache (TileMix abstract:
+ * INT8 key/value caches are supported).  The keys and values are
+ *   K^[s,hk,j,:] = k_scale[s,hk,j] * k8[s,hk,j,:],
+ *   V^[s,hk,j,:] = v_scale[s,hk,j] * v8[s,hk,j,:],
+ * and out is the attention of q over them:
+ *   FP16 route: S[i,j] = scale * <q[s,h,i,:], K^[s,hk,j,:]>
+ *   INT8 route: S[i,j] = scale * s_q[i] * k_scale[j] * <q8[s,h,i,:], k8[s,hk,j,:]>
+ * with q8, s_q the per-token codes of the query row (the rule above); the
+ * cached codes are the INT8 keys, not requantised.  Every other argument,
+ * the masks, the packed layout and the bitmask are those of attn_fwd.
+ *   k8, v8: device int8 in the layout of k and v; 16-byte aligned.
+ *   k_scale, v_scale: device fp32, one per K / V row ([B, n_kvh, ksl] dense,
+ *   [n_kvh, T] packed); 4-byte aligned.
+ * attn_quantize_rows builds such a cache from fp16 rows.  The value-cache
+ * scale is folded into the fp16 probabilities that multiply the codes, so
+ * p * v_scale must stay inside the fp16 range (v_scale = amax / 127 of a
+ * row well inside it does).  Errors as attn_fwd (ATTN_ERR_NULL names the
+ * cache pointers). */
+attn_status attn_fwd_kv8(const void* q, const int8_t* k8, const float* k_scale,
+                         const int8_t* v8, const float* v_scale, void* out,
+                         int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
+                         int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                         const int32_t* cu_seqlens, const uint32_t* route_bitmask,
+                         int32_t tiles_per_bit);
+
+/* Same, enqueued on hip_stream (a hipStream_t; NULL = null stream). */
+attn_status attn_fwd_kv8_stream(const void* q, const int8_t* k8, const float* k_scale,
+                                const int8_t* v8, const float* v_scale, void* out,
+                                int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
+                                int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                                const int32_t* cu_seqlens, const uint32_t* route_bitmask,
+                                int32_t tiles_per_bit, void* hip_stream);
+
+/* The INT8 cache encoder: per-token codes and scales (the rule above) of
+ * rows fp16 rows of hdim values.  x_f16: device [rows, hdim] fp16, 16-byte
+ * aligned; q8: device int8 [rows, hdim], 16-byte aligned; scale_out: device
+ * fp32 [rows], 4-byte aligned.  0 <= rows < 2^31.  Asynchronous on
+ * hip_stream. */
+attn_status attn_quantize_rows(const void* x_f16, int64_t rows, int32_t hdim, int8_t* q8,
+                               float* scale_out, void* hip_stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The string is owned by the library and valid until the next call. */

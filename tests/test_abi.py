@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for n in ["attn_fwd", "attn_fwd_stream", "attn_last_error", "attn_abi_version",
-              "attn_debug_quantize_rows", "attn_debug_route_dump"]:
+              "attn_debug_quantize_rows", "attn_debug_route_dump", "attn_fwd_kv8", "attn_fwd_kv8_stream",
+              "attn_quantize_rows"]:
         assert n in names
 
 
@@ -60,6 +61,34 @@ def call(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, qsl=64, ksl=64, hdim=64, n_qh=4,
 def test_validation_codes(kw, code):
     assert call(**kw) == code
     assert A.attn_last_error() != ""
+
+
+def call_kv8(q=FAKE, k8=FAKE, ks=FAKE, v8=FAKE, vs=FAKE, out=FAKE, B=1, qsl=64, ksl=64, hdim=64, n_qh=4,
+             n_kvh=2, scale=0.125, causal=0, cu=None, route=None, tpb=4):
+    lib = A.load()
+    return lib.attn_fwd_kv8(q, k8, ks, v8, vs, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal, cu, route, tpb)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k8=None), NULL), (dict(ks=None), NULL), (dict(v8=None), NULL),
+    (dict(vs=None), NULL), (dict(out=None), NULL),
+    (dict(qsl=0), SHAPE), (dict(n_qh=6, n_kvh=4), SHAPE), (dict(causal=1, qsl=65, ksl=64), SHAPE),
+    (dict(ksl=20000000, hdim=128), SHAPE),
+    (dict(hdim=96), UNSUP), (dict(scale=0.0), ARG), (dict(route=FAKE, tpb=0), ARG),
+    (dict(k8=FAKE + 8), ARG), (dict(v8=FAKE + 4), ARG), (dict(ks=FAKE + 2), ARG), (dict(vs=FAKE + 1), ARG),
+])
+def test_kv8_validation_codes(kw, code):
+    assert call_kv8(**kw) == code
+    assert A.attn_last_error() != ""
+
+
+def test_cache_encoder_validates():
+    lib = A.load()
+    assert lib.attn_quantize_rows(None, 4, 64, FAKE, FAKE, None) == NULL
+    assert lib.attn_quantize_rows(FAKE, -1, 64, FAKE, FAKE, None) == SHAPE
+    assert lib.attn_quantize_rows(FAKE, 1 << 31, 64, FAKE, FAKE, None) == SHAPE
+    assert lib.attn_quantize_rows(FAKE, 4, 80, FAKE, FAKE, None) == UNSUP
+    assert lib.attn_quantize_rows(FAKE + 4, 4, 64, FAKE, FAKE, None) == ARG
 
 
 def test_error_message_names_the_problem():

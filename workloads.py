@@ -16,7 +16,10 @@ Recipe: numpy.random.default_rng(seed).standard_normal in float64, drawn in
 the order Q, K, V, each cast to float16 with round-to-nearest-even.  The
 TileMix routing bitmask is a separate draw, default_rng(mask_seed).random(
 (n_qtiles, n_groups)) < p_int8, where a True bit selects the INT8 path, packed
-least-significant-bit first into rows of uint32 words.
+least-significant-bit first into rows of uint32 words.  Workloads marked kv8
+hand K and V over as an INT8 key/value cache: the same fp16 draws, encoded by
+the per-token quantiser of the side that consumes them (this module does no
+encoding).
 """
 from dataclasses import dataclass, field
 from typing import List, Optional
@@ -41,6 +44,7 @@ class Workload:
     tiles_per_bit: int = 0                    # 0: no routing bitmask
     mask_seed: int = 0
     p_int8: float = 0.5
+    kv8: bool = False                         # K and V as an INT8 key/value cache
     note: str = field(default="", compare=False)
 
     @property
@@ -65,6 +69,12 @@ WORKLOADS = {
                                           seed=41),
     "tilemix_16384_d128_causal": Workload("tilemix_16384_d128_causal", 1, 16384, 16384, 128, 32, 8, True,
                                           seed=5, tiles_per_bit=4, mask_seed=5005, p_int8=0.5),
+    # INT8 key/value cache inputs (TileMix abstract): the GQA and TileMix shapes
+    "gqa_4096_d128_causal_kv8": Workload("gqa_4096_d128_causal_kv8", 1, 4096, 4096, 128, 32, 8, True,
+                                         seed=3, kv8=True),
+    "tilemix_16384_d128_causal_kv8": Workload("tilemix_16384_d128_causal_kv8", 1, 16384, 16384, 128, 32, 8,
+                                              True, seed=5, tiles_per_bit=4, mask_seed=5005, p_int8=0.5,
+                                              kv8=True),
 }
 
 
