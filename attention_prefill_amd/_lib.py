@@ -56,6 +56,8 @@ def load():
         lib.attn_fwd_kv8_stream.restype = _I
         lib.attn_quantize_rows.argtypes = [_P, ctypes.c_int64, _I, _P, _P, _P]
         lib.attn_quantize_rows.restype = _I
+        lib.attn_fwd_unfused_stream.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]
+        lib.attn_fwd_unfused_stream.restype = _I
         _lib = lib
     return _lib
 
@@ -228,3 +230,21 @@ def attn_quantize_rows(x, stream=None):
     s = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     _check(load().attn_quantize_rows(_ptr(x), rows, d, _ptr(q8), _ptr(s), _stream(stream)))
     return q8, s
+
+
+def attn_fwd_unfused(q, k, v, out=None, *, scale=None, causal=False, stream=None):
+    """The unfused baseline (score GEMM, masked softmax, P.V GEMM) on dense
+    fp16 q [B, n_qh, qsl, d], k/v [B, n_kvh, ksl, d]; same result as attn_fwd."""
+    import torch
+    _need(q, "q", torch.float16)
+    _need(k, "k", torch.float16)
+    _need(v, "v", torch.float16)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    B, qsl, ksl, d, n_qh, n_kvh = _shapes(q, k, None)
+    out = _out_route(q, out, None)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    _check(load().attn_fwd_unfused_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, qsl, ksl, d, n_qh, n_kvh,
+                                          float(scale), int(bool(causal)), _stream(stream)))
+    return out

@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn_mi355x.so")
-SOURCES = ["attn_api.cpp", "attn_kernels.hip"]
+SOURCES = ["attn_api.cpp", "attn_kernels.hip", "attn_unfused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -41,7 +41,8 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError("hipcc failed")
     tmp = LIB + ".tmp%d" % os.getpid()
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
+                    "-L/opt/rocm/lib", "-lrocblas"], check=True)
     os.replace(tmp, LIB)
     return LIB
 

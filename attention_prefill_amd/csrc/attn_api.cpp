@@ -81,7 +81,7 @@ attn_status validate(const attn::Problem& p) {
 
 // Scratch comes from the device's default stream-ordered pool.  Its release
 // threshold is raised once per device so that freed blocks stay cached for
-// the next call instead of going back to the driver at every synchronise.
+// the next call instead of going back to the system at every synchronise.
 void keep_pool_cached() {
     static bool done[64] = {false};
     int dev = 0;
@@ -110,6 +110,27 @@ attn_status run_forward(const attn::Problem& p, hipStream_t st) {
         if (e == hipSuccess) e = e2;
     }
     if (e != hipSuccess) return hip_fail(e, "attention forward launch");
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
+// The unfused baseline: same validation, dense only, and a cap on the score
+// scratch (6 bytes per query-key pair).
+attn_status run_unfused(const attn::Problem& p, hipStream_t st) {
+    attn_status vs = validate(p);
+    if (vs != ATTN_OK) return vs;
+    const size_t bytes = attn::unfused_scratch_bytes(p);
+    if ((double)p.B * p.n_qh * p.qsl * p.ksl * 6.0 > 64.0e9)
+        return fail(ATTN_ERR_SHAPE, "unfused scores need %.1f GB of scratch (limit 64 GB)",
+                    (double)p.B * p.n_qh * p.qsl * p.ksl * 6.0 / 1e9);
+    keep_pool_cached();
+    void* scratch = nullptr;
+    hipError_t e = hipMallocAsync(&scratch, bytes, st);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of unfused scratch");
+    e = attn::launch_unfused(p, scratch, st);
+    hipError_t e2 = hipFreeAsync(scratch, st);
+    if (e == hipSuccess) e = e2;
+    if (e != hipSuccess) return hip_fail(e, "unfused attention");
     g_last_error.clear();
     return ATTN_OK;
 }
@@ -174,6 +195,13 @@ attn_status attn_fwd_kv8(const void* q, const int8_t* k8, const float* k_scale, 
                          const int32_t* cu_seqlens, const uint32_t* route_bitmask, int32_t tiles_per_bit) {
     return attn_fwd_kv8_stream(q, k8, k_scale, v8, v_scale, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal,
                                cu_seqlens, route_bitmask, tiles_per_bit, nullptr);
+}
+
+attn_status attn_fwd_unfused_stream(const void* q, const void* k, const void* v, void* out, int32_t B,
+                                    int32_t qsl, int32_t ksl, int32_t hdim, int32_t n_qh, int32_t n_kvh,
+                                    float scale, int32_t causal, void* hip_stream) {
+    attn::Problem p{q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal != 0, nullptr, nullptr, 1};
+    return run_unfused(p, (hipStream_t)hip_stream);
 }
 
 attn_status attn_quantize_rows(const void* x_f16, int64_t rows, int32_t hdim, int8_t* q8, float* scale_out,

@@ -34,6 +34,12 @@ size_t forward_scratch_bytes(const Problem& p);
 // forward_scratch_bytes(p) bytes (may be null when that is 0).
 hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t stream);
 
+// The unfused baseline: scores, a masked softmax and P.V as separate passes
+// (attn_unfused.hip).  Dense problems only; scratch holds the fp32 scores
+// and the fp16 probabilities.
+size_t unfused_scratch_bytes(const Problem& p);
+hipError_t launch_unfused(const Problem& p, void* scratch, hipStream_t stream);
+
 // Test hooks (include/attn.h).
 hipError_t launch_quantize_rows(const void* x, long long rows, int hdim, int8_t* q8, float* s,
                                 int path, hipStream_t stream);

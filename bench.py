@@ -63,6 +63,9 @@ def parse():
                     help="routed workloads: also time the same inputs with an all-FP16 (zero) "
                          "bitmask and with no bitmask; INT8-cache workloads: also time the "
                          "fp16 K and V the cache was encoded from")
+    ap.add_argument("--unfused-compare", action="store_true",
+                    help="dense fp16 workloads: also time the unfused baseline (score GEMM, masked "
+                         "softmax, P.V GEMM) on the same inputs, the page's t_unfs / speed_up")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (reference for HBM byte counters) and exit")
     return ap.parse_args()
@@ -88,6 +91,11 @@ class Call:
             # the INT8 key/value cache, encoded on the device before timing
             self.k8, self.sk = A.attn_quantize_rows(self.k)
             self.v8, self.sv = A.attn_quantize_rows(self.v)
+
+    def unfused(self, stream):
+        """The unfused baseline on the same dense fp16 inputs."""
+        self.A.attn_fwd_unfused(self.q, self.k, self.v, self.out, scale=self.w.scale, causal=self.w.causal,
+                                stream=stream)
 
     def __call__(self, stream, route="drawn", fp16_kv=False):
         """route: "drawn" (the workload's bitmask), "zero" (same kernel, every
@@ -291,6 +299,20 @@ def main():
         kv16_step = time_route("drawn", fp16_kv=True)
         rec["fp16_kv_ms_per_step"] = round(kv16_step * 1e3, 5)
         rec["kv8_speedup_vs_fp16_kv"] = round(kv16_step / sec_per_step, 4)
+    if args.unfused_compare and all(not c.w.varlen and not c.w.tiles_per_bit and not c.w.kv8 for c in calls):
+        # the page's other column: the same step through the unfused baseline
+        for _ in range(args.warmup):
+            for c in calls:
+                c.unfused(stream)
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for _ in range(args.steps):
+            for c in calls:
+                c.unfused(stream)
+        torch.cuda.synchronize()
+        unf_step = (time.perf_counter() - ta) / args.steps
+        rec["unfused_ms_per_step"] = round(unf_step * 1e3, 5)
+        rec["fused_speedup_vs_unfused"] = round(unf_step / sec_per_step, 3)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(calls)
     print(json.dumps(rec), flush=True)

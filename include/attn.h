@@ -121,6 +121,21 @@ attn_status attn_fwd_kv8_stream(const void* q, const int8_t* k8, const float* k_
                                 const int32_t* cu_seqlens, const uint32_t* route_bitmask,
                                 int32_t tiles_per_bit, void* hip_stream);
 
+/* The unfused baseline the "Nax Refactor" page times against its fused
+ * kernel (the t_unfs / speed_up columns of its timing tables): the same
+ * attention as attn_fwd for dense fp16 inputs (no packed batches, no
+ * bitmask), computed as separate passes over a materialised score matrix --
+ * S = Q K^T (rocBLAS strided-batched GEMM, fp32 scores), a masked row
+ * softmax (fp16 P), O = P V (GEMM, fp32 accumulation).  Arguments as
+ * attn_fwd.  Uses 6 bytes of stream-ordered scratch per (query, key) pair
+ * of the whole call; more than 64 GB is ATTN_ERR_SHAPE.  One rocBLAS handle
+ * per device is created on first use and kept; calls on one device
+ * serialise on it.  For comparison runs, not a production path. */
+attn_status attn_fwd_unfused_stream(const void* q, const void* k, const void* v, void* out,
+                                    int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
+                                    int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                                    void* hip_stream);
+
 /* The INT8 cache encoder: per-token codes and scales (the rule above) of
  * rows fp16 rows of hdim values.  x_f16: device [rows, hdim] fp16, 16-byte
  * aligned; q8: device int8 [rows, hdim], 16-byte aligned; scale_out: device

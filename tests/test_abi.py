@@ -27,7 +27,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for n in ["attn_fwd", "attn_fwd_stream", "attn_last_error", "attn_abi_version",
               "attn_debug_quantize_rows", "attn_debug_route_dump", "attn_fwd_kv8", "attn_fwd_kv8_stream",
-              "attn_quantize_rows"]:
+              "attn_quantize_rows", "attn_fwd_unfused_stream"]:
         assert n in names
 
 
@@ -79,6 +79,18 @@ def call_kv8(q=FAKE, k8=FAKE, ks=FAKE, v8=FAKE, vs=FAKE, out=FAKE, B=1, qsl=64, 
 ])
 def test_kv8_validation_codes(kw, code):
     assert call_kv8(**kw) == code
+    assert A.attn_last_error() != ""
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, FAKE, 1, 64, 64, 64, 4, 2, 0.1, 0), NULL),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 65, 64, 64, 4, 2, 0.1, 1), SHAPE),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 96, 4, 2, 0.1, 0), UNSUP),
+    ((FAKE, FAKE, FAKE, FAKE, 64, 16384, 16384, 128, 32, 8, 0.1, 0), SHAPE),   # 3.3 TB of scores
+    ((FAKE + 2, FAKE, FAKE, FAKE, 1, 64, 64, 64, 4, 2, 0.1, 0), ARG),
+])
+def test_unfused_validation_codes(args, code):
+    assert A.load().attn_fwd_unfused_stream(*args, None) == code
     assert A.attn_last_error() != ""
 
 
