@@ -54,6 +54,13 @@
  *    FP16 cells take the fp16 query against K^; INT8 cells take the
  *    quantised query against the cached codes (no second quantisation of
  *    K^); the output weights V^.
+ *  - FP8 route (oracle_attn_fwd_lowp with lowp = 1): a set routing bit
+ *    selects FP8 instead of INT8 for the whole call.  The format is e4m3
+ *    (bias 7, largest finite 448, no infinities) with rowwise dynamic
+ *    scaling read from "Add rowwise scaling to Float8Inference module":
+ *    s = fl32(amax/448), codes = e4m3 nearest to x * fl32(448/amax) (product
+ *    exact, ties to even, zero results +0); cells take
+ *    scale * s_q * s_k * sum_d e4m3(q) * e4m3(k), exact in fp64.
  *  - Output is the exact fp64 result; a fp16 round-to-nearest-even encoder
  *    is provided for exact special cases.
  *
@@ -147,6 +154,80 @@ void oracle_quantize_row(const uint16_t* x, int d, int8_t* q8, float* s_out)
 /* of adjacent key tiles).                                                 */
 /* ---------------------------------------------------------------------- */
 
+/* ---------------------------------------------------------------------- */
+/* FP8 e4m3 ("e4m3fn": sign, 4 exponent bits with bias 7, 3 mantissa bits; */
+/* no infinities; 0x7f and 0xff are NaN; largest finite value 448)         */
+/* ---------------------------------------------------------------------- */
+
+double oracle_e4m3_decode(uint8_t c)
+{
+    int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return (c & 0x80) ? -v : v;
+}
+
+/* The e4m3 value nearest to y, ties to the even mantissa, limited to +-448;
+ * a result of zero is +0.  The spacing of e4m3 values near |y| is
+ * 2^(e-3) with e = max(floor(log2|y|), -6) (the subnormal spacing is 2^-9). */
+double oracle_e4m3_round(double y)
+{
+    if (y == 0.0) return 0.0;
+    double a = fabs(y);
+    int E;
+    frexp(a, &E);                    /* a = f * 2^E, f in [0.5, 1) */
+    int e = E - 1;
+    if (e < -6) e = -6;
+    double q = ldexp(1.0, e - 3);
+    double r = nearbyint(a / q) * q; /* a / q is exact; nearbyint rounds ties to even */
+    if (r > 448.0) r = 448.0;
+    if (r == 0.0) return 0.0;
+    return y < 0 ? -r : r;
+}
+
+/* Bit pattern of an exact e4m3 value (zero encodes as 0x00). */
+uint8_t oracle_e4m3_encode(double r)
+{
+    if (r == 0.0) return 0;
+    double a = fabs(r);
+    int E;
+    frexp(a, &E);
+    int e = E - 1;
+    uint8_t code;
+    if (e < -6) {
+        code = (uint8_t)(a / ldexp(1.0, -9));                    /* subnormal: m * 2^-9 */
+    } else {
+        int m = (int)((a / ldexp(1.0, e) - 1.0) * 8.0);          /* (1 + m/8) * 2^e */
+        code = (uint8_t)(((e + 7) << 3) | m);
+    }
+    return (uint8_t)(code | (r < 0 ? 0x80 : 0));
+}
+
+/* Rowwise dynamic FP8 codes of one fp16 row ("Add rowwise scaling to
+ * Float8Inference module", rowwise / axiswise dynamic scaling, read with
+ * e4m3 and its largest finite value 448): amax = max |x|, s = fl32(amax/448),
+ * inv = fl32(448/amax), code = e4m3 nearest to x * inv (product exact); a
+ * zero row has s = 0 and codes 0. */
+void oracle_quantize_row_fp8(const uint16_t* x, int d, uint8_t* codes, float* s_out)
+{
+    float amax = 0.0f;
+    for (int t = 0; t < d; ++t) {
+        float a = (float)fabs(oracle_f16_to_f64(x[t]));
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        for (int t = 0; t < d; ++t) codes[t] = 0;
+        *s_out = 0.0f;
+        return;
+    }
+    volatile float num = 448.0f;     /* keep both divides as single fp32 ops */
+    float s = amax / num;
+    float inv = num / amax;
+    for (int t = 0; t < d; ++t)
+        codes[t] = oracle_e4m3_encode(oracle_e4m3_round(oracle_f16_to_f64(x[t]) * (double)inv));
+    *s_out = s;
+}
+
 /* Every row of an [rows, d] fp16 array, by oracle_quantize_row. */
 void oracle_quantize_rows(const uint16_t* x, long long rows, int d, int8_t* q8, float* s_out)
 {
@@ -180,6 +261,7 @@ typedef struct {
     const int32_t* cu;
     const uint32_t* route;
     int tiles_per_bit, tile_q, tile_k, wpr;
+    int lowp;                 /* what a set routing bit selects: 0 INT8, 1 FP8 e4m3 */
 } problem;
 
 /* Offsets of sequence s, head h in the dense [B,H,S,d] or packed [H,T,d]
@@ -238,6 +320,14 @@ static double val_val(const problem* p, size_t kb, int j, int t)
     return oracle_f16_to_f64(p->v[kb + (size_t)j * p->d + t]);
 }
 
+/* Codes of one row in the routed low-precision format (FP8 codes are kept as
+ * their bit patterns in the int8 array). */
+static void quantize_one(const problem* p, const uint16_t* x, int8_t* codes, float* s)
+{
+    if (p->lowp == 1) oracle_quantize_row_fp8(x, p->d, (uint8_t*)codes, s);
+    else oracle_quantize_row(x, p->d, codes, s);
+}
+
 /* Quantised rows for one (s, head) slab of L rows, or NULL when unrouted. */
 typedef struct { int8_t* q8; float* s; } qrows;
 
@@ -248,7 +338,7 @@ static qrows quantize_slab(const problem* p, const uint16_t* base, int L)
     r.q8 = (int8_t*)malloc((size_t)L * p->d);
     r.s = (float*)malloc((size_t)L * sizeof(float));
     for (int i = 0; i < L; ++i)
-        oracle_quantize_row(base + (size_t)i * p->d, p->d, r.q8 + (size_t)i * p->d, r.s + i);
+        quantize_one(p, base + (size_t)i * p->d, r.q8 + (size_t)i * p->d, r.s + i);
     return r;
 }
 
@@ -286,9 +376,19 @@ static void score_row(const problem* p, const uint16_t* qrow, size_t kb,
         if (int8_cell) {
             const int8_t* a = qq->q8 + (size_t)i * p->d;
             const int8_t* b = kq->q8 + (size_t)j * p->d;
-            int64_t dot = 0;
-            for (int t = 0; t < p->d; ++t) dot += (int64_t)a[t] * (int64_t)b[t];
-            S[j] = p->scale * (double)qq->s[i] * (double)kq->s[j] * (double)dot;
+            double dot;
+            if (p->lowp == 1) {
+                /* products of two e4m3 values have at most 8 significant bits
+                 * between 2^-18 and 2^18, so the fp64 sum is exact */
+                dot = 0.0;
+                for (int t = 0; t < p->d; ++t)
+                    dot += oracle_e4m3_decode((uint8_t)a[t]) * oracle_e4m3_decode((uint8_t)b[t]);
+            } else {
+                int64_t idot = 0;
+                for (int t = 0; t < p->d; ++t) idot += (int64_t)a[t] * (int64_t)b[t];
+                dot = (double)idot;
+            }
+            S[j] = p->scale * (double)qq->s[i] * (double)kq->s[j] * dot;
         } else {
             /* fp16 x fp16 and fp16 x (fp32 * int8) products are exact in fp64 */
             double acc = 0.0;
@@ -330,6 +430,8 @@ static int check_problem(const problem* p)
         for (int s = 0; s < p->B; ++s) if (p->cu[s + 1] < p->cu[s]) return ORACLE_ERR_ARG;
     }
     if (p->route && (p->tiles_per_bit < 1 || p->tile_q < 1 || p->tile_k < 1)) return ORACLE_ERR_ARG;
+    if (p->lowp != 0 && p->lowp != 1) return ORACLE_ERR_ARG;
+    if (p->lowp == 1 && p->k8) return ORACLE_ERR_ARG;   /* an INT8 cache has no FP8 codes */
     return 0;
 }
 
@@ -349,6 +451,7 @@ static problem make_problem(const uint16_t* q, const uint16_t* k, const uint16_t
     p.tile_q = tile_q > 0 ? tile_q : 64;
     p.tile_k = tile_k > 0 ? tile_k : 64;
     p.wpr = route ? oracle_route_words_per_row(ksl, p.tile_k, tiles_per_bit > 0 ? tiles_per_bit : 1) : 0;
+    p.lowp = 0;
     return p;
 }
 
@@ -438,7 +541,7 @@ static int run_rows(problem p, const int32_t* rows, int nrows, double* out, int 
             /* the row needs its own quantised Q row and every quantised K row */
             qq.q8 = (int8_t*)malloc((size_t)(i + 1) * d);
             qq.s = (float*)malloc((size_t)(i + 1) * sizeof(float));
-            oracle_quantize_row(q + qb + (size_t)i * d, d, qq.q8 + (size_t)i * d, qq.s + i);
+            quantize_one(&p, q + qb + (size_t)i * d, qq.q8 + (size_t)i * d, qq.s + i);
             kq = key_codes(&p, kb, Lk);
         }
         double* S = (double*)malloc((size_t)(Lk > 0 ? Lk : 1) * sizeof(double));
@@ -520,4 +623,31 @@ int oracle_attn_rows_kv8(const uint16_t* q, const int8_t* k8, const float* k_sca
     return run_rows(make_problem_kv8(q, k8, k_scale, v8, v_scale, B, qsl, ksl, d, n_qh, n_kvh,
                                      scale, causal, cu_seqlens, route, tiles_per_bit, tile_q, tile_k),
                     rows, nrows, out, nthreads);
+}
+
+/* The TileMix route with FP8 e4m3 as the low-precision format: cells whose
+ * bit is set take scale * s_q * s_k * sum_d e4m3(q8) * e4m3(k8) with the
+ * rowwise FP8 codes above (lowp = 1); lowp = 0 is oracle_attn_fwd. */
+int oracle_attn_fwd_lowp(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* out,
+                         int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                         float scale, int causal, const int32_t* cu_seqlens,
+                         const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                         int lowp, int nthreads)
+{
+    problem p = make_problem(q, k, v, B, qsl, ksl, d, n_qh, n_kvh, scale, causal,
+                             cu_seqlens, route, tiles_per_bit, tile_q, tile_k);
+    p.lowp = lowp;
+    return run_fwd(p, out, nthreads);
+}
+
+int oracle_attn_rows_lowp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                          float scale, int causal, const int32_t* cu_seqlens,
+                          const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                          int lowp, const int32_t* rows, int nrows, double* out, int nthreads)
+{
+    problem p = make_problem(q, k, v, B, qsl, ksl, d, n_qh, n_kvh, scale, causal,
+                             cu_seqlens, route, tiles_per_bit, tile_q, tile_k);
+    p.lowp = lowp;
+    return run_rows(p, rows, nrows, out, nthreads);
 }

@@ -25,6 +25,17 @@ uint16_t oracle_f64_to_f16_rne(double x);
 /* q8[0..d) and the fp32 scale s of one row x[0..d) of fp16 bits. */
 void oracle_quantize_row(const uint16_t* x, int d, int8_t* q8, float* s_out);
 
+/* FP8 e4m3 (sign, 4 exponent bits with bias 7, 3 mantissa bits, max 448):
+ * decode a bit pattern; round a value to the nearest e4m3 value (ties to
+ * even, zero results +0); encode an exact e4m3 value. */
+double  oracle_e4m3_decode(uint8_t c);
+double  oracle_e4m3_round(double y);
+uint8_t oracle_e4m3_encode(double r);
+
+/* Rowwise dynamic FP8 codes of one fp16 row: s = fl32(amax/448), codes the
+ * e4m3 values nearest to x * fl32(448/amax). */
+void oracle_quantize_row_fp8(const uint16_t* x, int d, uint8_t* codes, float* s_out);
+
 /* Every row of an [rows, d] fp16 array (the INT8 key/value cache encoder). */
 void oracle_quantize_rows(const uint16_t* x, long long rows, int d, int8_t* q8, float* s_out);
 
@@ -64,6 +75,20 @@ int oracle_attn_rows_kv8(const uint16_t* q, const int8_t* k8, const float* k_sca
                          float scale, int causal, const int32_t* cu_seqlens,
                          const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
                          const int32_t* rows, int nrows, double* out, int nthreads);
+
+/* lowp selects what a set routing bit means: 0 INT8 (as oracle_attn_fwd),
+ * 1 FP8 e4m3 with rowwise scales. */
+int oracle_attn_fwd_lowp(const uint16_t* q, const uint16_t* k, const uint16_t* v, double* out,
+                         int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                         float scale, int causal, const int32_t* cu_seqlens,
+                         const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                         int lowp, int nthreads);
+
+int oracle_attn_rows_lowp(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          int B, int qsl, int ksl, int d, int n_qh, int n_kvh,
+                          float scale, int causal, const int32_t* cu_seqlens,
+                          const uint32_t* route, int tiles_per_bit, int tile_q, int tile_k,
+                          int lowp, const int32_t* rows, int nrows, double* out, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -43,6 +43,18 @@ def _load():
         lib.oracle_attn_fwd.restype = _I
         lib.oracle_attn_rows.argtypes = common + shape + [_P, _I, _P, _I]
         lib.oracle_attn_rows.restype = _I
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = ctypes.c_double
+        lib.oracle_e4m3_round.argtypes = [ctypes.c_double]
+        lib.oracle_e4m3_round.restype = ctypes.c_double
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_quantize_row_fp8.argtypes = [_P, _I, _P, _P]
+        lib.oracle_quantize_row_fp8.restype = None
+        lib.oracle_attn_fwd_lowp.argtypes = common + [_P] + shape + [_I, _I]
+        lib.oracle_attn_fwd_lowp.restype = _I
+        lib.oracle_attn_rows_lowp.argtypes = common + shape + [_I, _P, _I, _P, _I]
+        lib.oracle_attn_rows_lowp.restype = _I
         cache = [_P, _P, _P, _P, _P]
         lib.oracle_attn_fwd_kv8.argtypes = cache + [_P] + shape + [_I]
         lib.oracle_attn_fwd_kv8.restype = _I
@@ -118,32 +130,36 @@ def _common(q, k, v, cu_seqlens, route):
     return qb, kb, vb, cu, rt
 
 
+_LOWP = {"int8": 0, "fp8": 1}
+
+
 def attn_fwd(q, k, v, *, scale, causal=False, cu_seqlens=None, route=None,
-             tiles_per_bit=4, tile_q=64, tile_k=64, nthreads=0) -> np.ndarray:
-    """The exact fp64 attention output, same shape as q."""
+             tiles_per_bit=4, tile_q=64, tile_k=64, lowp="int8", nthreads=0) -> np.ndarray:
+    """The exact fp64 attention output, same shape as q.  lowp: the format a
+    set routing bit selects ("int8", or "fp8" for e4m3 with rowwise scales)."""
     qb, kb, vb, cu, rt = _common(q, k, v, cu_seqlens, route)
     B, qsl, ksl, d, n_qh, n_kvh = _shape_args(qb, kb, cu)
     out = np.zeros(qb.shape, dtype=np.float64)
-    rc = _load().oracle_attn_fwd(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(out), B, qsl, ksl, d, n_qh,
-                                 n_kvh, float(np.float32(scale)), int(bool(causal)), _ptr(cu),
-                                 _ptr(rt), int(tiles_per_bit), int(tile_q), int(tile_k),
-                                 int(nthreads))
+    rc = _load().oracle_attn_fwd_lowp(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(out), B, qsl, ksl, d, n_qh,
+                                      n_kvh, float(np.float32(scale)), int(bool(causal)), _ptr(cu),
+                                      _ptr(rt), int(tiles_per_bit), int(tile_q), int(tile_k),
+                                      _LOWP[lowp], int(nthreads))
     if rc != 0:
         raise ValueError("oracle_attn_fwd rejected its arguments (code %d)" % rc)
     return out
 
 
 def attn_rows(q, k, v, rows, *, scale, causal=False, cu_seqlens=None, route=None,
-              tiles_per_bit=4, tile_q=64, tile_k=64, nthreads=0) -> np.ndarray:
+              tiles_per_bit=4, tile_q=64, tile_k=64, lowp="int8", nthreads=0) -> np.ndarray:
     """Output rows for the (s, h, i) triples in rows, as float64 [len(rows), d]."""
     qb, kb, vb, cu, rt = _common(q, k, v, cu_seqlens, route)
     B, qsl, ksl, d, n_qh, n_kvh = _shape_args(qb, kb, cu)
     r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
     out = np.zeros((r.shape[0], d), dtype=np.float64)
-    rc = _load().oracle_attn_rows(_ptr(qb), _ptr(kb), _ptr(vb), B, qsl, ksl, d, n_qh, n_kvh,
-                                  float(np.float32(scale)), int(bool(causal)), _ptr(cu), _ptr(rt),
-                                  int(tiles_per_bit), int(tile_q), int(tile_k), _ptr(r),
-                                  r.shape[0], _ptr(out), int(nthreads))
+    rc = _load().oracle_attn_rows_lowp(_ptr(qb), _ptr(kb), _ptr(vb), B, qsl, ksl, d, n_qh, n_kvh,
+                                       float(np.float32(scale)), int(bool(causal)), _ptr(cu), _ptr(rt),
+                                       int(tiles_per_bit), int(tile_q), int(tile_k), _LOWP[lowp], _ptr(r),
+                                       r.shape[0], _ptr(out), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_attn_rows rejected its arguments (code %d)" % rc)
     return out
@@ -203,3 +219,25 @@ def attn_rows_kv8(q, k8, k_scale, v8, v_scale, rows, *, scale, causal=False, cu_
     if rc != 0:
         raise ValueError("oracle_attn_rows_kv8 rejected its arguments (code %d)" % rc)
     return out
+
+
+def e4m3_decode(code: int) -> float:
+    return _load().oracle_e4m3_decode(int(code))
+
+
+def e4m3_round(y: float) -> float:
+    """The e4m3 value nearest to y (ties to even, zero results +0)."""
+    return _load().oracle_e4m3_round(float(y))
+
+
+def e4m3_encode(r: float) -> int:
+    return int(_load().oracle_e4m3_encode(float(r)))
+
+
+def quantize_row_fp8(x: np.ndarray):
+    """(codes uint8[d] e4m3 bit patterns, s float32) of one fp16 row."""
+    xb = _bits(x)
+    c = np.zeros(xb.shape[0], dtype=np.uint8)
+    s = np.zeros(1, dtype=np.float32)
+    _load().oracle_quantize_row_fp8(_ptr(xb), xb.shape[0], _ptr(c), _ptr(s))
+    return c, np.float32(s[0])
