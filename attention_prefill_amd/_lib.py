@@ -56,6 +56,8 @@ def load():
         lib.attn_fwd_kv8_stream.restype = _I
         lib.attn_quantize_rows.argtypes = [_P, ctypes.c_int64, _I, _P, _P, _P]
         lib.attn_quantize_rows.restype = _I
+        lib.attn_fwd_lowp_stream.argtypes = fwd_args + [_I, _P]
+        lib.attn_fwd_lowp_stream.restype = _I
         lib.attn_fwd_unfused_stream.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]
         lib.attn_fwd_unfused_stream.restype = _I
         _lib = lib
@@ -140,13 +142,17 @@ def _out_route(q, out, route_bitmask):
     return out
 
 
+LOWP = {"int8": 0, "fp8": 1}
+
+
 def attn_fwd(q, k, v, out=None, *, scale=None, causal=False, cu_seqlens=None,
-             route_bitmask=None, tiles_per_bit=4, stream=None):
+             route_bitmask=None, tiles_per_bit=4, lowp="int8", stream=None):
     """Fused attention forward; sizes are read from the tensor shapes.
 
     dense:  q [B, n_qh, qsl, d], k/v [B, n_kvh, ksl, d]
     packed: q [n_qh, T, d], k/v [n_kvh, T, d], cu_seqlens int32 [B + 1]
     route_bitmask: int32 / uint32-valued tensor of packed routing words.
+    lowp: what a set routing bit selects, "int8" or "fp8" (e4m3, rowwise scales).
     Returns out (allocated when None).  Enqueued on torch's current stream.
     """
     import torch
@@ -159,9 +165,22 @@ def attn_fwd(q, k, v, out=None, *, scale=None, causal=False, cu_seqlens=None,
     out = _out_route(q, out, route_bitmask)
     if scale is None:
         scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
-    attn_fwd_stream(q, k, v, out, B, qsl, ksl, d, n_qh, n_kvh, scale, causal, cu_seqlens,
-                    route_bitmask, tiles_per_bit, stream)
+    if lowp == "int8":
+        attn_fwd_stream(q, k, v, out, B, qsl, ksl, d, n_qh, n_kvh, scale, causal, cu_seqlens,
+                        route_bitmask, tiles_per_bit, stream)
+    else:
+        attn_fwd_lowp_stream(q, k, v, out, B, qsl, ksl, d, n_qh, n_kvh, scale, causal, cu_seqlens,
+                             route_bitmask, tiles_per_bit, LOWP[lowp], stream)
     return out
+
+
+def attn_fwd_lowp_stream(q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal,
+                         cu_seqlens=None, route_bitmask=None, tiles_per_bit=4, lowp_format=0, stream=None):
+    """Direct mirror of the C entry point (sizes passed explicitly)."""
+    _check(load().attn_fwd_lowp_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, qsl, ksl, hdim, n_qh,
+                                       n_kvh, float(scale), int(bool(causal)), _ptr(cu_seqlens),
+                                       _ptr(route_bitmask), int(tiles_per_bit), int(lowp_format),
+                                       _stream(stream)))
 
 
 def attn_debug_quantize_rows(x, path=0, stream=None):

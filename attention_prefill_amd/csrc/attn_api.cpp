@@ -59,6 +59,10 @@ attn_status validate(const attn::Problem& p) {
         return fail(ATTN_ERR_ARG, "scale must be finite and non-zero");
     if (p.route && p.tiles_per_bit < 1)
         return fail(ATTN_ERR_ARG, "tiles_per_bit must be >= 1 with a bitmask (got %d)", p.tiles_per_bit);
+    if (p.lowp != ATTN_LOWP_INT8 && p.lowp != ATTN_LOWP_FP8_E4M3)
+        return fail(ATTN_ERR_ARG, "lowp_format must be ATTN_LOWP_INT8 or ATTN_LOWP_FP8_E4M3 (got %d)", p.lowp);
+    if (p.lowp == ATTN_LOWP_FP8_E4M3 && kv8)
+        return fail(ATTN_ERR_UNSUPPORTED, "an INT8 key/value cache has no FP8 codes");
     if (kv8) {
         if (!aligned16(p.q) || !aligned16(p.k8) || !aligned16(p.v8) || !aligned16(p.out))
             return fail(ATTN_ERR_ARG, "q, k8, v8 and out must be 16-byte aligned");
@@ -173,6 +177,17 @@ const char* attn_last_error(void) { return g_last_error.c_str(); }
 
 int32_t attn_abi_version(void) { return ATTN_ABI_VERSION; }
 
+attn_status attn_fwd_lowp_stream(const void* q, const void* k, const void* v, void* out, int32_t B,
+                                 int32_t qsl, int32_t ksl, int32_t hdim, int32_t n_qh, int32_t n_kvh,
+                                 float scale, int32_t causal, const int32_t* cu_seqlens,
+                                 const uint32_t* route_bitmask, int32_t tiles_per_bit, int32_t lowp_format,
+                                 void* hip_stream) {
+    attn::Problem p{q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal != 0,
+                    cu_seqlens, route_bitmask, tiles_per_bit};
+    p.lowp = lowp_format;
+    return run_forward(p, (hipStream_t)hip_stream);
+}
+
 attn_status attn_fwd_kv8_stream(const void* q, const int8_t* k8, const float* k_scale, const int8_t* v8,
                                 const float* v_scale, void* out, int32_t B, int32_t qsl, int32_t ksl,
                                 int32_t hdim, int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
@@ -211,7 +226,7 @@ attn_status attn_quantize_rows(const void* x_f16, int64_t rows, int32_t hdim, in
 
 attn_status attn_debug_quantize_rows(const void* x_f16, int32_t rows, int32_t hdim, int8_t* q8,
                                      float* scale_out, int32_t path, void* hip_stream) {
-    if (path != 0 && path != 1) return fail(ATTN_ERR_ARG, "path must be 0 or 1");
+    if (path < 0 || path > 3) return fail(ATTN_ERR_ARG, "path must be 0, 1, 2 or 3");
     return quantize_rows(x_f16, (long long)rows, hdim, q8, scale_out, path, (hipStream_t)hip_stream);
 }
 

@@ -24,6 +24,8 @@ struct Problem {
     const float* k_scale = nullptr;
     const int8_t* v8 = nullptr;
     const float* v_scale = nullptr;
+    // what a set routing bit selects: 0 INT8, 1 FP8 e4m3 (rowwise scales)
+    int lowp = 0;
 };
 
 // Device scratch a forward call needs (bytes): quantised K rows for routed
@@ -40,7 +42,8 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t stream);
 size_t unfused_scratch_bytes(const Problem& p);
 hipError_t launch_unfused(const Problem& p, void* scratch, hipStream_t stream);
 
-// Test hooks (include/attn.h).
+// Quantisers (include/attn.h): path 0 K-row pass INT8, 1 query prologue
+// INT8, 2 K-row pass FP8, 3 query prologue FP8.
 hipError_t launch_quantize_rows(const void* x, long long rows, int hdim, int8_t* q8, float* s,
                                 int path, hipStream_t stream);
 hipError_t launch_route_dump(const uint32_t* route, int qsl, int ksl, bool causal,

@@ -59,6 +59,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -101,6 +102,39 @@ __device__ __forceinline__ int quant_code(float x, float inv) {
     return (int)r;
 }
 
+// FP8 route: e4m3 codes with rowwise scales, s = fl32(amax/448) and
+// code = the e4m3 value nearest to x * fl32(448/amax) (product exact, ties to
+// even).  Near |y| the e4m3 spacing is 2^(e-3), e = max(floor(log2|y|), -6);
+// adding C = 1.5 * 2^(e+20), whose fp32 spacing is that same 2^(e-3), in one
+// fused multiply-add rounds the exact product once to that spacing, and
+// subtracting C leaves the e4m3 value (|y| <= 448 keeps e <= 8).  A product
+// that rounds up across a power of two in fl32(x * inv) picks the larger
+// spacing, which yields the same power of two.  Zero results are +0.
+__device__ __forceinline__ float fp8_round(float x, float inv) {
+    const float hi = x * inv;
+    int e = (int)((__builtin_bit_cast(unsigned, hi) >> 23) & 0xffu) - 127;
+    e = e < -6 ? -6 : e;
+    const float C = __builtin_bit_cast(float, ((unsigned)(e + 147) << 23) | 0x400000u);
+    return __builtin_fmaf(x, inv, C) - C;
+}
+
+// Four e4m3 codes (exact values, so the conversion does not round), byte b = v[b].
+__device__ __forceinline__ unsigned fp8_pack4(float v0, float v1, float v2, float v3) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+    return (unsigned)w;
+}
+
+__device__ __forceinline__ void fp8_scale(float amax, float& s, float& inv) {
+    if (amax == 0.0f) {
+        s = 0.0f;
+        inv = 0.0f;
+    } else {
+        s = amax / 448.0f;
+        inv = 448.0f / amax;
+    }
+}
+
 __device__ __forceinline__ float f_from_u(unsigned u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ unsigned u_from_f(float f) { return __builtin_bit_cast(unsigned, f); }
 
@@ -118,7 +152,9 @@ __device__ __forceinline__ float halfwave_sum(float v) {
 // Query rows held in the score B-operand layout: lane l (g = l/32) holds
 // Q[row l%32][32*kb + 16*g + 8*e + j] in qf[2*kb + e][j].  The INT8 operand
 // for k-step ks holds the 16 codes of d = 32*ks + 16*g + j, j = 0..15.
-template <int HD>
+// FP8 codes use the same byte positions; an FP8 MFMA operand (64 values)
+// is the pair of INT8 operands ks = 2k, 2k+1.
+template <int HD, bool FP8 = false>
 __device__ __forceinline__ void quantize_q_regs(const f16x8 (&qf)[HD / 16], i32x4 (&q8)[HD / 32],
                                                 float& s_out) {
     float amax = 0.0f;
@@ -128,19 +164,30 @@ __device__ __forceinline__ void quantize_q_regs(const f16x8 (&qf)[HD / 16], i32x
         for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)qf[t][j]));
     amax = halfwave_max(amax);
     float s, inv;
-    quant_scale(amax, s, inv);
+    if constexpr (FP8) fp8_scale(amax, s, inv);
+    else quant_scale(amax, s, inv);
 #pragma unroll
     for (int ks = 0; ks < HD / 32; ++ks) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            unsigned word = 0;
+            if constexpr (FP8) {
+                float r[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                int j = 4 * w + b;
-                int c = quant_code((float)qf[2 * ks + j / 8][j % 8], inv);
-                word |= ((unsigned)c & 0xffu) << (8 * b);
+                for (int b = 0; b < 4; ++b) {
+                    const int j = 4 * w + b;
+                    r[b] = fp8_round((float)qf[2 * ks + j / 8][j % 8], inv);
+                }
+                q8[ks][w] = (int)fp8_pack4(r[0], r[1], r[2], r[3]);
+            } else {
+                unsigned word = 0;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    int j = 4 * w + b;
+                    int c = quant_code((float)qf[2 * ks + j / 8][j % 8], inv);
+                    word |= ((unsigned)c & 0xffu) << (8 * b);
+                }
+                q8[ks][w] = (int)word;
             }
-            q8[ks][w] = (int)word;
         }
     }
     s_out = s;
@@ -221,7 +268,7 @@ constexpr float TAU = 8.0f;
 // ---------------------------------------------------------------------------
 // Fused forward kernel.
 // ---------------------------------------------------------------------------
-template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8>
+template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8, bool FP8>
 __global__ __launch_bounds__(NW * KS * 64, (NW == 2 || KS > 1) ? 1 : (BN == 32 ? 3 : 2))
 void attn_fwd_kernel(FwdArgs a) {
     using L = Lds<HD>;
@@ -590,7 +637,28 @@ void attn_fwd_kernel(FwdArgs a) {
                 x[kb32][12 + i] *= s3[i];
             }
         };
-        if (ROUTED && i8) {
+        if (ROUTED && i8 && FP8) {
+            // v_mfma_f32_32x32x64_f8f6f4 with both formats e4m3 and no block
+            // scales; operand k = 64 values = the INT8 operands 2k and 2k+1
+#pragma unroll
+            for (int kb32 = 0; kb32 < NKB; ++kb32) {
+                f32x16 acc = f32x16{};
+                const int8_t* kr = (const int8_t*)kbuf + (32 * kb32 + krow) * L::K8P + 16 * g;
+#pragma unroll
+                for (int k2 = 0; k2 < HD / 64; ++k2) {
+                    const i32x4 a0 = *(const i32x4*)(kr + 64 * k2);
+                    const i32x4 a1 = *(const i32x4*)(kr + 64 * k2 + 32);
+                    const i32x8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                    const i32x4 b0 = q8[2 * k2], b1 = q8[2 * k2 + 1];
+                    const i32x8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) x[kb32][i] = acc[i];
+                key_scale(kb32);
+            }
+            amul = sq_mul;
+        } else if (ROUTED && i8) {
 #pragma unroll
             for (int kb32 = 0; kb32 < NKB; ++kb32) {
                 i32x16 acc = i32x16{};
@@ -759,7 +827,7 @@ void attn_fwd_kernel(FwdArgs a) {
     }
     if constexpr (ROUTED) {
         float sq;
-        quantize_q_regs<HD>(qf, q8, sq);
+        quantize_q_regs<HD, FP8>(qf, q8, sq);
         sq_mul = sq > 0.0f ? sq : 1.0f;   // a zero row has all-zero INT8 scores
     }
     if constexpr (PF == 2) lstore2(set0, 0);
@@ -892,7 +960,7 @@ void attn_fwd_kernel(FwdArgs a) {
 // K-row quantisation pass (and test hook path 0): rows of HD fp16 values,
 // HD/8 lanes per row, 8 values per lane.
 // ---------------------------------------------------------------------------
-template <int HD>
+template <int HD, bool FP8 = false>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const _Float16* __restrict__ x,
                                                             int8_t* __restrict__ q8,
                                                             float* __restrict__ s, long long rows) {
@@ -908,12 +976,20 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const _Float16* __re
 #pragma unroll
     for (int o = 1; o < LPR; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     float sc, inv;
-    quant_scale(amax, sc, inv);
     unsigned w0 = 0, w1 = 0;
+    if constexpr (FP8) {
+        fp8_scale(amax, sc, inv);
+        w0 = fp8_pack4(fp8_round((float)v[0], inv), fp8_round((float)v[1], inv), fp8_round((float)v[2], inv),
+                       fp8_round((float)v[3], inv));
+        w1 = fp8_pack4(fp8_round((float)v[4], inv), fp8_round((float)v[5], inv), fp8_round((float)v[6], inv),
+                       fp8_round((float)v[7], inv));
+    } else {
+        quant_scale(amax, sc, inv);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        w0 |= ((unsigned)quant_code((float)v[j], inv) & 0xffu) << (8 * j);
-        w1 |= ((unsigned)quant_code((float)v[4 + j], inv) & 0xffu) << (8 * j);
+        for (int j = 0; j < 4; ++j) {
+            w0 |= ((unsigned)quant_code((float)v[j], inv) & 0xffu) << (8 * j);
+            w1 |= ((unsigned)quant_code((float)v[4 + j], inv) & 0xffu) << (8 * j);
+        }
     }
     if (ok) {
         *(uint2*)(q8 + row * HD + part * 8) = uint2{w0, w1};
@@ -960,7 +1036,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(const float* __restri
 }
 
 // Test hook path 1: the query prologue quantiser on 32-row blocks.
-template <int HD>
+template <int HD, bool FP8 = false>
 __global__ __launch_bounds__(64) void quantize_qrows_kernel(const _Float16* __restrict__ x,
                                                             int8_t* __restrict__ q8,
                                                             float* __restrict__ s, int rows) {
@@ -975,7 +1051,7 @@ __global__ __launch_bounds__(64) void quantize_qrows_kernel(const _Float16* __re
     }
     i32x4 q8r[HD / 32];
     float sc;
-    quantize_q_regs<HD>(qf, q8r, sc);
+    quantize_q_regs<HD, FP8>(qf, q8r, sc);
     if (row < rows) {
 #pragma unroll
         for (int ks = 0; ks < HD / 32; ++ks)
@@ -1004,9 +1080,9 @@ hipError_t set_lds(K kernel, int bytes) {
     return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8>
+template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8, bool FP8>
 hipError_t launch_fwd_t(const FwdArgs& a, int grid, hipStream_t st) {
-    auto kern = attn_fwd_kernel<HD, NW, KS, CAUSAL, VARLEN, ROUTED, KV8>;
+    auto kern = attn_fwd_kernel<HD, NW, KS, CAUSAL, VARLEN, ROUTED, KV8, FP8>;
     constexpr int lds = Lds<HD>::TOTAL * KS;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
@@ -1014,22 +1090,25 @@ hipError_t launch_fwd_t(const FwdArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int HD, int NW, int KS, bool ROUTED, bool KV8>
+template <int HD, int NW, int KS, bool ROUTED, bool KV8, bool FP8 = false>
 hipError_t dispatch_mask(const FwdArgs& a, int grid, bool causal, bool varlen, hipStream_t st) {
     if (varlen)
-        return causal ? launch_fwd_t<HD, NW, KS, true, true, ROUTED, KV8>(a, grid, st)
-                      : launch_fwd_t<HD, NW, KS, false, true, ROUTED, KV8>(a, grid, st);
-    return causal ? launch_fwd_t<HD, NW, KS, true, false, ROUTED, KV8>(a, grid, st)
-                  : launch_fwd_t<HD, NW, KS, false, false, ROUTED, KV8>(a, grid, st);
+        return causal ? launch_fwd_t<HD, NW, KS, true, true, ROUTED, KV8, FP8>(a, grid, st)
+                      : launch_fwd_t<HD, NW, KS, false, true, ROUTED, KV8, FP8>(a, grid, st);
+    return causal ? launch_fwd_t<HD, NW, KS, true, false, ROUTED, KV8, FP8>(a, grid, st)
+                  : launch_fwd_t<HD, NW, KS, false, false, ROUTED, KV8, FP8>(a, grid, st);
 }
 
 // Instantiated shapes: two-wave workgroups for routed calls with an odd head
-// group only, two key groups for non-routed FP16 calls only.
+// group only, two key groups for non-routed FP16 calls only, FP8 routes on
+// fp16 inputs only.
 template <int HD>
 hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, bool varlen, bool routed,
-                    bool kv8, hipStream_t st) {
+                    bool kv8, bool fp8, hipStream_t st) {
+    if (fp8 && (!routed || kv8 || KS != 1)) return hipErrorInvalidConfiguration;
     if (NW == 2) {
         if (!routed || KS != 1) return hipErrorInvalidConfiguration;
+        if (fp8) return dispatch_mask<HD, 2, 1, true, false, true>(a, grid, causal, varlen, st);
         return kv8 ? dispatch_mask<HD, 2, 1, true, true>(a, grid, causal, varlen, st)
                    : dispatch_mask<HD, 2, 1, true, false>(a, grid, causal, varlen, st);
     }
@@ -1037,9 +1116,11 @@ hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, boo
         if (routed || kv8) return hipErrorInvalidConfiguration;
         return dispatch_mask<HD, 4, 2, false, false>(a, grid, causal, varlen, st);
     }
-    if (routed)
+    if (routed) {
+        if (fp8) return dispatch_mask<HD, 4, 1, true, false, true>(a, grid, causal, varlen, st);
         return kv8 ? dispatch_mask<HD, 4, 1, true, true>(a, grid, causal, varlen, st)
                    : dispatch_mask<HD, 4, 1, true, false>(a, grid, causal, varlen, st);
+    }
     return kv8 ? dispatch_mask<HD, 4, 1, false, true>(a, grid, causal, varlen, st)
                : dispatch_mask<HD, 4, 1, false, false>(a, grid, causal, varlen, st);
 }
@@ -1050,23 +1131,20 @@ hipError_t launch_quantize_rows(const void* x, long long rows, int hdim, int8_t*
                                 int path, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
     if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (path == 0) {
+    const _Float16* xh = (const _Float16*)x;
+    if (path == 0 || path == 2) {
+        // K-row pass: INT8 (0) or FP8 (2)
         const long long threads = (long long)rows * (hdim / 8);
         const int grid = (int)((threads + 255) / 256);
-        if (hdim == 64)
-            hipLaunchKernelGGL(quantize_rows_kernel<64>, dim3(grid), dim3(256), 0, st,
-                               (const _Float16*)x, q8, s, (long long)rows);
-        else
-            hipLaunchKernelGGL(quantize_rows_kernel<128>, dim3(grid), dim3(256), 0, st,
-                               (const _Float16*)x, q8, s, (long long)rows);
+        auto k = hdim == 64 ? (path == 0 ? quantize_rows_kernel<64, false> : quantize_rows_kernel<64, true>)
+                            : (path == 0 ? quantize_rows_kernel<128, false> : quantize_rows_kernel<128, true>);
+        hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, st, xh, q8, s, rows);
     } else {
+        // query-prologue quantiser: INT8 (1) or FP8 (3)
         const int grid = (int)((rows + 31) / 32);
-        if (hdim == 64)
-            hipLaunchKernelGGL(quantize_qrows_kernel<64>, dim3(grid), dim3(64), 0, st,
-                               (const _Float16*)x, q8, s, (int)rows);
-        else
-            hipLaunchKernelGGL(quantize_qrows_kernel<128>, dim3(grid), dim3(64), 0, st,
-                               (const _Float16*)x, q8, s, (int)rows);
+        auto k = hdim == 64 ? (path == 1 ? quantize_qrows_kernel<64, false> : quantize_qrows_kernel<64, true>)
+                            : (path == 1 ? quantize_qrows_kernel<128, false> : quantize_qrows_kernel<128, true>);
+        hipLaunchKernelGGL(k, dim3(grid), dim3(64), 0, st, xh, q8, s, (int)rows);
     }
     return hipGetLastError();
 }
@@ -1210,7 +1288,8 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
             const size_t krows = varlen ? (size_t)p.n_kvh * p.ksl : (size_t)p.B * p.n_kvh * p.ksl;
             a.k8 = (const int8_t*)((char*)scratch + pl.k8_off);
             a.sk = (const float*)((char*)scratch + pl.sk_off);
-            hipError_t e = launch_quantize_rows(p.k, (long long)krows, p.hdim, (int8_t*)a.k8, (float*)a.sk, 0, st);
+            hipError_t e = launch_quantize_rows(p.k, (long long)krows, p.hdim, (int8_t*)a.k8, (float*)a.sk,
+                                                p.lowp == 1 ? 2 : 0, st);
             if (e != hipSuccess) return e;
         }
     } else {
@@ -1221,10 +1300,11 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
     if (pl.grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const int grid = (int)pl.grid;
     hipError_t e;
+    const bool fp8 = routed && p.lowp == 1;
     if (p.hdim == 64)
-        e = dispatch<64>(a, grid, pl.NW, pl.KS, p.causal, varlen, routed, kv8, st);
+        e = dispatch<64>(a, grid, pl.NW, pl.KS, p.causal, varlen, routed, kv8, fp8, st);
     else
-        e = dispatch<128>(a, grid, pl.NW, pl.KS, p.causal, varlen, routed, kv8, st);
+        e = dispatch<128>(a, grid, pl.NW, pl.KS, p.causal, varlen, routed, kv8, fp8, st);
     if (e != hipSuccess || pl.ksplit == 1) return e;
     const long long threads = pl.out_rows * (p.hdim / 8);
     const int mgrid = (int)((threads + 255) / 256);

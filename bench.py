@@ -109,6 +109,11 @@ class Call:
                                        w.hdim, w.n_qh, w.n_kvh, w.scale, w.causal, self.cu, rt,
                                        w.tiles_per_bit or 4, stream)
             return
+        if w.lowp != "int8" and rt is not None:
+            self.A.attn_fwd_lowp_stream(self.q, self.k, self.v, self.out, B, w.qsl, w.ksl, w.hdim, w.n_qh,
+                                        w.n_kvh, w.scale, w.causal, self.cu, rt, w.tiles_per_bit or 4,
+                                        self.A._lib.LOWP[w.lowp], stream)
+            return
         self.A.attn_fwd_stream(self.q, self.k, self.v, self.out, B, w.qsl, w.ksl, w.hdim, w.n_qh,
                                w.n_kvh, w.scale, w.causal, self.cu, rt, w.tiles_per_bit or 4, stream)
 
@@ -149,7 +154,7 @@ def cpu_baseline(calls, budget_s=12.0):
             else:
                 oracle.attn_fwd(np.ascontiguousarray(qs), np.ascontiguousarray(ks), np.ascontiguousarray(vs),
                                 scale=w.scale, causal=w.causal, cu_seqlens=cu, route=c.route_host,
-                                tiles_per_bit=w.tiles_per_bit or 4, nthreads=threads)
+                                tiles_per_bit=w.tiles_per_bit or 4, lowp=w.lowp, nthreads=threads)
             spent += time.perf_counter() - t0
             heads += 1
         flop += c.metric_flop * heads / w.n_qh
@@ -241,7 +246,8 @@ def main():
     dw = dc.w
     dom_name = "attn_fwd_kernel hd%d %s%s%s%s" % (dw.hdim, "causal" if dw.causal else "noncausal",
                                                    " varlen" if dw.varlen else "",
-                                                   " routed" if dw.tiles_per_bit else "",
+                                                   (" routed" + (" fp8" if dw.lowp == "fp8" else ""))
+                                                   if dw.tiles_per_bit else "",
                                                    " kv8" if dw.kv8 else "")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP16_PEAK_TFLOPS, 4),
@@ -264,6 +270,7 @@ def main():
            "ksl": w0.ksl, "hdim": w0.hdim, "n_qh": w0.n_qh, "n_kvh": w0.n_kvh,
            "causal": [c.w.causal for c in calls] if len(calls) > 1 else w0.causal,
            "seqlens": w0.seqlens, "tiles_per_bit": w0.tiles_per_bit or None, "kv_cache_int8": w0.kv8,
+           "low_precision_route": w0.lowp if w0.tiles_per_bit else None,
            "calls_per_step": len(calls)}
     rec = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 5),

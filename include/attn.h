@@ -73,6 +73,12 @@ typedef enum {
 
 #define ATTN_ABI_VERSION 1
 
+/* The format a set routing bit selects (attn_fwd_lowp_stream). */
+typedef enum {
+    ATTN_LOWP_INT8 = 0,      /* per-token INT8, the rule above (attn_fwd's route) */
+    ATTN_LOWP_FP8_E4M3 = 1   /* per-token FP8 e4m3, rowwise dynamic scaling */
+} attn_lowp;
+
 /* Fused attention forward on the null (default) stream.  scale may be
  * negative; tiles_per_bit is read only when route_bitmask != NULL. */
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* out,
@@ -144,6 +150,24 @@ attn_status attn_fwd_unfused_stream(const void* q, const void* k, const void* v,
 attn_status attn_quantize_rows(const void* x_f16, int64_t rows, int32_t hdim, int8_t* q8,
                                float* scale_out, void* hip_stream);
 
+/* The TileMix route with a choice of low-precision format for the groups
+ * whose bit is set.  lowp_format ATTN_LOWP_INT8 is attn_fwd_stream.
+ * ATTN_LOWP_FP8_E4M3 takes the rowwise dynamic scaling of the "Add rowwise
+ * scaling to Float8Inference module" page (one scale per row from its
+ * absolute maximum) with e4m3 codes (sign, 4 exponent bits biased by 7, 3
+ * mantissa bits, largest finite 448; the FP8 MFMA of gfx950 runs at the
+ * INT8 rate):
+ *   s = fl32(amax / 448), code = the e4m3 value nearest to x * fl32(448 / amax)
+ *   (product exact, ties to the even mantissa; a zero row has s = 0, codes 0),
+ *   S[i,j] = scale * s_q[i] * s_k[j] * sum_d e4m3(q)[i,d] * e4m3(k)[j,d].
+ * Other arguments and errors as attn_fwd_stream; any other lowp_format is
+ * ATTN_ERR_ARG. */
+attn_status attn_fwd_lowp_stream(const void* q, const void* k, const void* v, void* out,
+                                 int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
+                                 int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                                 const int32_t* cu_seqlens, const uint32_t* route_bitmask,
+                                 int32_t tiles_per_bit, int32_t lowp_format, void* hip_stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The string is owned by the library and valid until the next call. */
 const char* attn_last_error(void);
@@ -151,10 +175,11 @@ const char* attn_last_error(void);
 /* ATTN_ABI_VERSION of the loaded library. */
 int32_t attn_abi_version(void);
 
-/* Test hooks for bit-exact checks of the INT8 quantiser (same rule as above).
- * x_f16: device [rows, hdim] fp16; q8: device int8 [rows, hdim]; scale_out:
- * device fp32 [rows].  path 0 runs the K-row quantiser used before routed
- * calls, path 1 the query-row quantiser of the attention prologue.
+/* Test hooks for bit-exact checks of the quantisers (rules above).
+ * x_f16: device [rows, hdim] fp16; q8: device int8 [rows, hdim] (FP8 paths:
+ * e4m3 bit patterns); scale_out: device fp32 [rows].  path 0 runs the INT8
+ * K-row quantiser used before routed calls, path 1 the INT8 query-row
+ * quantiser of the attention prologue, paths 2 and 3 the same two for FP8.
  * Asynchronous on hip_stream. */
 attn_status attn_debug_quantize_rows(const void* x_f16, int32_t rows, int32_t hdim,
                                      int8_t* q8, float* scale_out, int32_t path,

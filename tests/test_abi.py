@@ -27,7 +27,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for n in ["attn_fwd", "attn_fwd_stream", "attn_last_error", "attn_abi_version",
               "attn_debug_quantize_rows", "attn_debug_route_dump", "attn_fwd_kv8", "attn_fwd_kv8_stream",
-              "attn_quantize_rows", "attn_fwd_unfused_stream"]:
+              "attn_quantize_rows", "attn_fwd_unfused_stream", "attn_fwd_lowp_stream"]:
         assert n in names
 
 
@@ -92,6 +92,17 @@ def test_kv8_validation_codes(kw, code):
 def test_unfused_validation_codes(args, code):
     assert A.load().attn_fwd_unfused_stream(*args, None) == code
     assert A.attn_last_error() != ""
+
+
+def test_lowp_format_validation():
+    lib = A.load()
+    args = (FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 4, 2, 0.125, 0, None, FAKE, 4)
+    assert lib.attn_fwd_lowp_stream(*args, 2, None) == ARG
+    assert lib.attn_fwd_lowp_stream(*args, -1, None) == ARG
+    assert "lowp" in A.attn_last_error()
+    assert lib.attn_fwd_lowp_stream(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 96, 4, 2, 0.125, 0, None, FAKE, 4,
+                                    1, None) == UNSUP
+    assert lib.attn_debug_quantize_rows(FAKE, 4, 64, FAKE, FAKE, 4, None) == ARG
 
 
 def test_cache_encoder_validates():

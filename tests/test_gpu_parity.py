@@ -384,7 +384,7 @@ def gather(out, rows, varlen, cu):
     return np.stack([out[b, h, i] for (b, h, i) in rows])
 
 
-@pytest.mark.parametrize("name", [n for n, w in W.WORKLOADS.items() if not w.kv8])
+@pytest.mark.parametrize("name", [n for n, w in W.WORKLOADS.items() if not w.kv8 and w.lowp == "int8"])
 def test_workload_full_size(A, orc, name):
     w = W.WORKLOADS[name]
     say("workload", name)

@@ -45,6 +45,7 @@ class Workload:
     mask_seed: int = 0
     p_int8: float = 0.5
     kv8: bool = False                         # K and V as an INT8 key/value cache
+    lowp: str = "int8"                        # what a set routing bit selects: "int8" or "fp8"
     note: str = field(default="", compare=False)
 
     @property
@@ -69,6 +70,9 @@ WORKLOADS = {
                                           seed=41),
     "tilemix_16384_d128_causal": Workload("tilemix_16384_d128_causal", 1, 16384, 16384, 128, 32, 8, True,
                                           seed=5, tiles_per_bit=4, mask_seed=5005, p_int8=0.5),
+    # the TileMix shape with FP8 e4m3 (rowwise scales) as the low-precision route
+    "tilemix_16384_d128_causal_fp8": Workload("tilemix_16384_d128_causal_fp8", 1, 16384, 16384, 128, 32, 8, True,
+                                              seed=5, tiles_per_bit=4, mask_seed=5005, p_int8=0.5, lowp="fp8"),
     # INT8 key/value cache inputs (TileMix abstract): the GQA and TileMix shapes
     "gqa_4096_d128_causal_kv8": Workload("gqa_4096_d128_causal_kv8", 1, 4096, 4096, 128, 32, 8, True,
                                          seed=3, kv8=True),
