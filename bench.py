@@ -164,9 +164,10 @@ def cpu_baseline(calls, budget_s=12.0):
             "sample": "; ".join(samples) + ", full sequence length, same inputs; %.1f s" % secs}
 
 
-def hbm_traffic(dominant_name):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None when the kernel source changed since it was taken."""
+def hbm_traffic(workload, dominant_name):
+    """HBM bytes per launch of the dominant kernel of this workload from the
+    committed counter summary, or None when the counters were not taken on
+    this workload or the kernel source changed since they were."""
     try:
         with open(COUNTERS_FILE) as f:
             rec = json.load(f)
@@ -174,7 +175,7 @@ def hbm_traffic(dominant_name):
             sha = hashlib.sha256(f.read()).hexdigest()
         if rec.get("kernel_source_sha256") != sha:
             return None
-        ent = rec["kernels"].get(dominant_name)
+        ent = rec["workloads"].get(workload, {}).get(dominant_name)
         if not ent:
             return None
         return ent["fetch_kib"] * 1024.0 * rec["fetch_scale"] + ent["write_kib"] * 1024.0 * rec["write_scale"]
@@ -251,7 +252,7 @@ def main():
                                                    " kv8" if dw.kv8 else "")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP16_PEAK_TFLOPS, 4),
-                "traffic": hbm_traffic(dom_name), "kernel": dom_name,
+                "traffic": hbm_traffic(args.workload, dom_name), "kernel": dom_name,
                 "flop_per_launch": dc.visited_flop, "avg_launch_ms": round(dom_ms, 5)}
 
     # the page's figures for the same shapes, combined like the value
