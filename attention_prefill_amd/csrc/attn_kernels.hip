@@ -269,7 +269,7 @@ constexpr float TAU = 8.0f;
 // Fused forward kernel.
 // ---------------------------------------------------------------------------
 template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8, bool FP8>
-__global__ __launch_bounds__(NW * KS * 64, (NW == 2 || KS > 1) ? 1 : (BN == 32 ? 3 : 2))
+__global__ __launch_bounds__(NW * KS * 64, (NW != 4 || KS > 1) ? 1 : (BN == 32 ? 3 : 2))
 void attn_fwd_kernel(FwdArgs a) {
     using L = Lds<HD>;
     constexpr int NT = NW * 64;                        // threads of one key group
@@ -1100,8 +1100,8 @@ hipError_t dispatch_mask(const FwdArgs& a, int grid, bool causal, bool varlen, h
 }
 
 // Instantiated shapes: two-wave workgroups for routed calls with an odd head
-// group only, two key groups for non-routed FP16 calls only, FP8 routes on
-// fp16 inputs only.
+// group only, two key groups and eight query wavefronts for non-routed fp16
+// calls only, FP8 routes on fp16 inputs only.
 template <int HD>
 hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, bool varlen, bool routed,
                     bool kv8, bool fp8, hipStream_t st) {
@@ -1115,6 +1115,10 @@ hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, boo
     if (KS == 2) {
         if (routed || kv8) return hipErrorInvalidConfiguration;
         return dispatch_mask<HD, 4, 2, false, false>(a, grid, causal, varlen, st);
+    }
+    if (NW == 8) {
+        if (routed || kv8 || KS != 1) return hipErrorInvalidConfiguration;
+        return dispatch_mask<HD, 8, 1, false, false>(a, grid, causal, varlen, st);
     }
     if (routed) {
         if (fp8) return dispatch_mask<HD, 4, 1, true, false, true>(a, grid, causal, varlen, st);
@@ -1197,30 +1201,48 @@ static Plan make_plan(const Problem& p) {
     const bool routed = p.route != nullptr;
     const bool kv8 = p.k8 != nullptr;
     const int G = p.n_qh / p.n_kvh;
-    // workgroup shape: a routed workgroup stays inside one 64-row query tile
-    pl.NW = 4;
+    const long long simds = 4LL * cu_count();
+    const int n_kt = (p.ksl + BN - 1) / BN;
     pl.HPW = largest_div(G, 4);
-    if (routed && pl.HPW == 1) pl.NW = 2;
-    pl.BM = (pl.NW / pl.HPW) * 32;
+    auto blocks_of = [&](int nw) {        // query-row blocks per workgroup column
+        const int bm = (nw / pl.HPW) * 32;
+        return varlen ? (p.qsl + bm - 1) / bm + p.B : (p.qsl + bm - 1) / bm;
+    };
+    // key-range splits that bring w wavefronts to two per SIMD, keeping at
+    // least sixteen tiles per split (the fp32 partials and their merge cost
+    // more than they return otherwise)
+    auto splits_for = [&](long long w) {
+        int ks = 1;
+        while (ks < 8 && w * ks < 2 * simds && n_kt >= 16 * ks) ks *= 2;
+        return ks;
+    };
     pl.combos = (varlen ? 1 : p.B) * p.n_kvh * (G / pl.HPW);
-    pl.n_mblk = varlen ? (p.qsl + pl.BM - 1) / pl.BM + p.B : (p.qsl + pl.BM - 1) / pl.BM;
+    // Workgroup shape.  A routed workgroup stays inside one 64-row query tile
+    // (two wavefronts when the head group is odd).  Unrouted fp16 calls whose
+    // grid gives two wavefronts per SIMD even so take eight query wavefronts:
+    // each K/V tile then serves twice the rows, halving the tile loads and
+    // LDS stores per FLOP.  (With fewer, four wavefronts and two key groups
+    // hide latency better than eight and a split key range.)
+    pl.NW = 4;
+    if (routed && pl.HPW == 1) pl.NW = 2;
+    if (!routed && !kv8 && (long long)pl.combos * blocks_of(8) * 8 >= 2 * simds) pl.NW = 8;
+    const char* force_nw = getenv("ATTN_QUERY_WAVES");
+    if (!routed && !kv8 && force_nw && (force_nw[0] == '4' || force_nw[0] == '8') && force_nw[1] == 0)
+        pl.NW = force_nw[0] - '0';
+    pl.BM = (pl.NW / pl.HPW) * 32;
+    pl.n_mblk = blocks_of(pl.NW);
     // Small grids leave SIMDs with one wavefront or none, so nothing hides
     // the latency of one wavefront's loads, softmax and MFMA chains.  First
     // give each workgroup a second key group (same rows, alternate key tiles,
     // merged in LDS); then, if SIMDs are still idle, split the key range over
-    // workgroups (fp32 partials and a merge pass, which cost more than they
-    // return otherwise): up to two wavefronts per SIMD, keeping at least
-    // sixteen tiles per split.
+    // workgroups: up to two wavefronts per SIMD.
     const long long waves = (long long)pl.combos * pl.n_mblk * pl.NW;
-    const long long simds = 4LL * cu_count();
-    const int n_kt = (p.ksl + BN - 1) / BN;
     const bool kg2_ok = !routed && !kv8 && pl.NW == 4;
     pl.KS = (kg2_ok && waves < 2 * simds && n_kt >= 2) ? 2 : 1;
     const char* force_kg = getenv("ATTN_KEY_GROUPS");
     if (kg2_ok && force_kg && (force_kg[0] == '1' || force_kg[0] == '2') && force_kg[1] == 0)
         pl.KS = force_kg[0] - '0';
-    int ks = 1;
-    while (ks < 8 && waves * pl.KS * ks < 2 * simds && n_kt >= 16 * ks) ks *= 2;
+    int ks = splits_for(waves * pl.KS);
     const char* force = getenv("ATTN_KSPLIT");
     if (force && force[0] >= '1' && force[0] <= '8' && force[1] == 0) ks = force[0] - '0';
     pl.ksplit = ks;

@@ -99,6 +99,7 @@ def test_gpu_fp8_varlen_and_all_fp8(A, orc, d, causal):
 
 def test_gpu_fp8_zero_mask_is_dense_bitexact(A, monkeypatch):
     monkeypatch.setenv("ATTN_KEY_GROUPS", "1")
+    monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
     rng = np.random.default_rng(1990)
     q, k, v = rand16(rng, (1, 8, 300, 128)), rand16(rng, (1, 2, 300, 128)), rand16(rng, (1, 2, 300, 128))
     zeros = W.pack_bits(np.zeros((5, 2), dtype=bool))

@@ -70,13 +70,18 @@ def rand16(rng, shape):
 SHAPES = [(1, 1), (5, 70), (64, 64), (65, 65), (130, 130), (200, 333), (333, 200), (300, 1000)]
 
 
-@pytest.fixture(params=["1", "2"], ids=["kg1", "kg2"])
+@pytest.fixture(params=["kg1", "kg2", "nw8"])
 def key_groups(request, monkeypatch):
-    """Both workgroup shapes of non-routed calls: one key group, or two key
-    groups that take alternate key tiles and merge in LDS (what small grids
-    get by default)."""
-    monkeypatch.setenv("ATTN_KEY_GROUPS", request.param)
-    return int(request.param)
+    """The workgroup shapes of non-routed calls: four query wavefronts with one
+    key group, or with two key groups that take alternate key tiles and merge
+    in LDS (what small grids get by default), or eight query wavefronts (what
+    large grids get)."""
+    if request.param == "nw8":
+        monkeypatch.setenv("ATTN_QUERY_WAVES", "8")
+        return 8
+    monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
+    monkeypatch.setenv("ATTN_KEY_GROUPS", request.param[2])
+    return int(request.param[2])
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -88,7 +93,7 @@ def test_dense_ragged(A, orc, d, heads, causal, key_groups):
         if causal and qsl > ksl:
             continue
         B = 2 if qsl <= 70 else 1
-        say("dense d=%d heads=%s causal=%d B=%d qsl=%d ksl=%d kg=%d" % (d, heads, causal, B, qsl, ksl, key_groups))
+        say("dense d=%d heads=%s causal=%d B=%d qsl=%d ksl=%d shape=%d" % (d, heads, causal, B, qsl, ksl, key_groups))
         q, k, v = rand16(rng, (B, heads[0], qsl, d)), rand16(rng, (B, heads[1], ksl, d)), \
             rand16(rng, (B, heads[1], ksl, d))
         scale = float(np.float32(1 / np.sqrt(d)))
@@ -105,7 +110,7 @@ def test_varlen_ragged(A, orc, d, heads, causal, key_groups):
     lens = [1, 63, 64, 65, 200, 0, 130, 7]
     cu = W.cu_seqlens_of(lens)
     T = int(cu[-1])
-    say("varlen d=%d heads=%s causal=%d lens=%s kg=%d" % (d, heads, causal, lens, key_groups))
+    say("varlen d=%d heads=%s causal=%d lens=%s shape=%d" % (d, heads, causal, lens, key_groups))
     q, k, v = rand16(rng, (heads[0], T, d)), rand16(rng, (heads[1], T, d)), rand16(rng, (heads[1], T, d))
     got = gpu_attn(A, q, k, v, 0.1, causal, cu=cu)
     ref = orc.attn_fwd(q, k, v, scale=0.1, causal=causal, cu_seqlens=cu)
@@ -152,8 +157,10 @@ def test_routed_varlen_ragged(A, orc, d, heads, causal, tpb):
 
 
 def test_gpu_routed_varlen_zero_mask_is_dense(A, monkeypatch):
-    """Routed calls run one key group; the dense call is pinned to the same shape."""
+    """Routed calls run four query wavefronts and one key group; the dense call
+    is pinned to the same shape."""
     monkeypatch.setenv("ATTN_KEY_GROUPS", "1")
+    monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
     rng = np.random.default_rng(510)
     lens = [100, 1, 250, 64]
     cu = W.cu_seqlens_of(lens)
@@ -229,8 +236,10 @@ def test_gpu_rows_sum_to_one(A, routed):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_gpu_all_zero_mask_is_dense_bitexact(A, d, monkeypatch):
-    """Routed calls run one key group; the dense call is pinned to the same shape."""
+    """Routed calls run four query wavefronts and one key group; the dense call
+    is pinned to the same shape."""
     monkeypatch.setenv("ATTN_KEY_GROUPS", "1")
+    monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
     rng = np.random.default_rng(63)
     q, k, v = rand16(rng, (1, 8, 300, d)), rand16(rng, (1, 2, 300, d)), rand16(rng, (1, 2, 300, d))
     zeros = W.pack_bits(np.zeros((5, 2), dtype=bool))
@@ -240,10 +249,10 @@ def test_gpu_all_zero_mask_is_dense_bitexact(A, d, monkeypatch):
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
-@pytest.mark.parametrize("kg", ["1", "2"])
+@pytest.mark.parametrize("kg", ["1", "2", "nw8"])
 def test_gpu_varlen_equals_separate_calls(A, monkeypatch, kg):
-    """Same tiling (fixed key groups, no split over workgroups): bit-identical;
-    default launch plans: within fp16 rounding."""
+    """Same tiling (fixed workgroup shape, no split over workgroups):
+    bit-identical; default launch plans: within fp16 rounding."""
     rng = np.random.default_rng(64)
     lens = [70, 1, 129, 300]
     cu = W.cu_seqlens_of(lens)
@@ -251,7 +260,11 @@ def test_gpu_varlen_equals_separate_calls(A, monkeypatch, kg):
     q, k, v = rand16(rng, (8, T, 128)), rand16(rng, (2, T, 128)), rand16(rng, (2, T, 128))
     packed = gpu_attn(A, q, k, v, 0.1, True, cu=cu)
     monkeypatch.setenv("ATTN_KSPLIT", "1")
-    monkeypatch.setenv("ATTN_KEY_GROUPS", kg)
+    if kg == "nw8":
+        monkeypatch.setenv("ATTN_QUERY_WAVES", "8")
+    else:
+        monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
+        monkeypatch.setenv("ATTN_KEY_GROUPS", kg)
     packed1 = gpu_attn(A, q, k, v, 0.1, True, cu=cu)
     for s in range(len(lens)):
         a, b = cu[s], cu[s + 1]
