@@ -13,7 +13,9 @@
 //     head.  With KS = 2 a second group of NW wavefronts owns the same rows
 //     and takes every other key tile; the two online-softmax states merge
 //     through LDS at the end (small grids get two wavefronts per SIMD this
-//     way without a second pass).  Grid order is heavy-first for causal
+//     way without a second pass; small causal grids use NW = 2, two
+//     workgroups per CU, so heavy and light query blocks share CUs).
+//     Grid order is heavy-first for causal
 //     masks and keeps the workgroups of one kv head on one XCD (index mod 8)
 //     when the number of head groups is a multiple of 8.
 //   * tile loader: 64-key K and V tiles go global -> registers -> LDS
@@ -269,7 +271,7 @@ constexpr float TAU = 8.0f;
 // Fused forward kernel.
 // ---------------------------------------------------------------------------
 template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8, bool FP8>
-__global__ __launch_bounds__(NW * KS * 64, (NW != 4 || KS > 1) ? 1 : (BN == 32 ? 3 : 2))
+__global__ __launch_bounds__(NW * KS * 64, (NW == 2 && KS == 2) ? 2 : (NW != 4 || KS > 1) ? 1 : (BN == 32 ? 3 : 2))
 void attn_fwd_kernel(FwdArgs a) {
     using L = Lds<HD>;
     constexpr int NT = NW * 64;                        // threads of one key group
@@ -1099,13 +1101,18 @@ hipError_t dispatch_mask(const FwdArgs& a, int grid, bool causal, bool varlen, h
                   : launch_fwd_t<HD, NW, KS, false, false, ROUTED, KV8, FP8>(a, grid, st);
 }
 
-// Instantiated shapes: two-wave workgroups for routed calls with an odd head
-// group only, two key groups and eight query wavefronts for non-routed fp16
-// calls only, FP8 routes on fp16 inputs only.
+// Instantiated shapes: two query wavefronts with one key group for routed
+// calls with an odd head group, and with two key groups for small non-routed
+// fp16 grids; two key groups and eight query wavefronts for non-routed fp16
+// calls only; FP8 routes on fp16 inputs only.
 template <int HD>
 hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, bool varlen, bool routed,
                     bool kv8, bool fp8, hipStream_t st) {
     if (fp8 && (!routed || kv8 || KS != 1)) return hipErrorInvalidConfiguration;
+    if (NW == 2 && KS == 2) {
+        if (routed || kv8) return hipErrorInvalidConfiguration;
+        return dispatch_mask<HD, 2, 2, false, false>(a, grid, causal, varlen, st);
+    }
     if (NW == 2) {
         if (!routed || KS != 1) return hipErrorInvalidConfiguration;
         if (fp8) return dispatch_mask<HD, 2, 1, true, false, true>(a, grid, causal, varlen, st);
@@ -1226,9 +1233,28 @@ static Plan make_plan(const Problem& p) {
     pl.NW = 4;
     if (routed && pl.HPW == 1) pl.NW = 2;
     if (!routed && !kv8 && (long long)pl.combos * blocks_of(8) * 8 >= 2 * simds) pl.NW = 8;
+    // Small fp16 grids (under two wavefronts per SIMD) run one workgroup per
+    // CU.  Under a causal mask whose diagonal spans most of the keys, the
+    // workgroups of the last query rows visit every key tile and those of the
+    // first rows almost none, so the launch lasts as long as its heaviest
+    // workgroup; a grid with fewer workgroups than CUs leaves CUs idle.  Both
+    // take 64-row workgroups of two query wavefronts and two key groups, two
+    // per CU, so a heavy block shares its CU with a light one.  (Only where
+    // the head group already fits two wavefronts: splitting a larger group
+    // halves the rows each K/V tile serves, and at hdim 128 two such
+    // workgroups exceed the CU's LDS.)
+    const bool fp16_small = !routed && !kv8 && p.hdim == 64 && pl.HPW <= 2 && n_kt >= 2 &&
+                            (long long)pl.combos * blocks_of(4) * 4 < 2 * simds;
+    const bool diag = p.causal && p.ksl - p.qsl < p.qsl;
+    if (pl.NW == 4 && fp16_small && (diag || (long long)pl.combos * blocks_of(4) < simds / 4)) pl.NW = 2;
     const char* force_nw = getenv("ATTN_QUERY_WAVES");
-    if (!routed && !kv8 && force_nw && (force_nw[0] == '4' || force_nw[0] == '8') && force_nw[1] == 0)
+    if (!routed && !kv8 && force_nw && (force_nw[0] == '2' || force_nw[0] == '4' || force_nw[0] == '8') &&
+        force_nw[1] == 0)
         pl.NW = force_nw[0] - '0';
+    if (pl.NW == 2 && !routed && pl.HPW > 2) {
+        pl.HPW = largest_div(G, 2);
+        pl.combos = (varlen ? 1 : p.B) * p.n_kvh * (G / pl.HPW);
+    }
     pl.BM = (pl.NW / pl.HPW) * 32;
     pl.n_mblk = blocks_of(pl.NW);
     // Small grids leave SIMDs with one wavefront or none, so nothing hides
@@ -1242,6 +1268,7 @@ static Plan make_plan(const Problem& p) {
     const char* force_kg = getenv("ATTN_KEY_GROUPS");
     if (kg2_ok && force_kg && (force_kg[0] == '1' || force_kg[0] == '2') && force_kg[1] == 0)
         pl.KS = force_kg[0] - '0';
+    if (pl.NW == 2 && !routed) pl.KS = 2;     // the only non-routed two-wavefront shape
     int ks = splits_for(waves * pl.KS);
     const char* force = getenv("ATTN_KSPLIT");
     if (force && force[0] >= '1' && force[0] <= '8' && force[1] == 0) ks = force[0] - '0';

@@ -70,15 +70,16 @@ def rand16(rng, shape):
 SHAPES = [(1, 1), (5, 70), (64, 64), (65, 65), (130, 130), (200, 333), (333, 200), (300, 1000)]
 
 
-@pytest.fixture(params=["kg1", "kg2", "nw8"])
+@pytest.fixture(params=["kg1", "kg2", "nw8", "nw2"])
 def key_groups(request, monkeypatch):
     """The workgroup shapes of non-routed calls: four query wavefronts with one
     key group, or with two key groups that take alternate key tiles and merge
-    in LDS (what small grids get by default), or eight query wavefronts (what
-    large grids get)."""
-    if request.param == "nw8":
-        monkeypatch.setenv("ATTN_QUERY_WAVES", "8")
-        return 8
+    in LDS (what small grids get by default), eight query wavefronts (what
+    large grids get), or two query wavefronts with two key groups (what small
+    causal hdim-64 grids get; larger head groups are split in pairs)."""
+    if request.param in ("nw8", "nw2"):
+        monkeypatch.setenv("ATTN_QUERY_WAVES", request.param[2])
+        return int(request.param[2]) * 10
     monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
     monkeypatch.setenv("ATTN_KEY_GROUPS", request.param[2])
     return int(request.param[2])
@@ -249,7 +250,7 @@ def test_gpu_all_zero_mask_is_dense_bitexact(A, d, monkeypatch):
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
-@pytest.mark.parametrize("kg", ["1", "2", "nw8"])
+@pytest.mark.parametrize("kg", ["1", "2", "nw8", "nw2"])
 def test_gpu_varlen_equals_separate_calls(A, monkeypatch, kg):
     """Same tiling (fixed workgroup shape, no split over workgroups):
     bit-identical; default launch plans: within fp16 rounding."""
@@ -260,8 +261,8 @@ def test_gpu_varlen_equals_separate_calls(A, monkeypatch, kg):
     q, k, v = rand16(rng, (8, T, 128)), rand16(rng, (2, T, 128)), rand16(rng, (2, T, 128))
     packed = gpu_attn(A, q, k, v, 0.1, True, cu=cu)
     monkeypatch.setenv("ATTN_KSPLIT", "1")
-    if kg == "nw8":
-        monkeypatch.setenv("ATTN_QUERY_WAVES", "8")
+    if kg in ("nw8", "nw2"):
+        monkeypatch.setenv("ATTN_QUERY_WAVES", kg[2])
     else:
         monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
         monkeypatch.setenv("ATTN_KEY_GROUPS", kg)
