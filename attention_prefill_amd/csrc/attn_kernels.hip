@@ -362,11 +362,8 @@ void attn_fwd_kernel(FwdArgs a) {
     const int w_nkt = !wave_active ? 0
                     : CAUSAL ? min(n_kt, (min(r0 + 31, Lq - 1) + off) / BN + 1) : n_kt;
 
+    // this workgroup's row of the routing bitmask (one 64-row query tile)
     const uint32_t* rrow = ROUTED ? a.route + (size_t)(rrow0 + m0 / TQ) * a.wpr : nullptr;
-    // route of kernel tile kt: the bit of its 64-key routing tile
-    auto tile_i8 = [&](int kt) __attribute__((always_inline)) {
-        return route_bit(rrow, (kt * BN) / TK, a.tiles_per_bit);
-    };
 
     // ---- query rows into the score B-operand layout ---------------------------
     const int qi = r0 + lq;
@@ -809,40 +806,96 @@ void attn_fwd_kernel(FwdArgs a) {
     const int it_full = max(0, (min(nfull, kt1) - kt0) / KS);
     const int kt_first = kt0 + kgp;
     auto has = [&](int it) __attribute__((always_inline)) { return it < n_it && kt_first + KS * it < kt1; };
-    auto i8_of = [&](int it) __attribute__((always_inline)) {
-        return ROUTED && has(it) && tile_i8(kt_first + KS * it);
-    };
 
+    const int kt_end = min(w_nkt, kt1);
+    auto query_prologue = [&]() __attribute__((always_inline)) {
+        if (a.neg) {
+#pragma unroll
+            for (int t = 0; t < HD / 16; ++t) qf[t] = -qf[t];
+        }
+        if constexpr (ROUTED) {
+            float sq;
+            quantize_q_regs<HD, FP8>(qf, q8, sq);
+            sq_mul = sq > 0.0f ? sq : 1.0f;   // a zero row has all-zero INT8 scores
+        }
+    };
+    if constexpr (ROUTED) {
+        // Routed calls take their tiles in two passes, first every FP16 tile
+        // and then every low-precision tile, each in key order, so that each
+        // pass runs a loop body specialised for its route (the online-softmax
+        // state does not depend on the order of the tiles).  The bitmask word
+        // in use is cached; a new word is read every 32 groups.
+        static_assert(KS == 1 && PF == 1 && BN == TK, "routed calls: one key group of 64-key tiles");
+        const int tpb = a.tiles_per_bit;
+        int wi_c = -1;
+        uint32_t w_c = 0;
+        // first tile >= t of this workgroup's range whose route is c, else kt1
+        auto next_of = [&](int t, bool c) __attribute__((always_inline)) {
+            while (t < kt1) {
+                const int gi = __builtin_amdgcn_readfirstlane(t / tpb);
+                if ((gi >> 5) != wi_c) {
+                    wi_c = gi >> 5;
+                    w_c = __builtin_amdgcn_readfirstlane(rrow[wi_c]);
+                }
+                const uint32_t wv = (c ? w_c : ~w_c) >> (gi & 31);
+                if (wv) return min(kt1, max(t, (gi + (int)__builtin_ctz(wv)) * tpb));
+                t = (wi_c + 1) * 32 * tpb;
+            }
+            return kt1;
+        };
+        int st = 0;
+        // tiles [kt, kt1) of route C, the first (kt) already in LDS stage st
+        auto pass = [&](auto cls_tag, int kt) __attribute__((always_inline)) {
+            constexpr bool C = decltype(cls_tag)::value;
+            int kn = next_of(kt + 1, C);
+            auto step = [&](auto mask_tag) __attribute__((always_inline)) {
+                constexpr bool MASK = decltype(mask_tag)::value;
+                if (kn < kt1) gload(set0, kn, C);
+                if (MASK ? kt < kt_end : wave_active) tile(mask_tag, st, kt, C);
+                if (kn < kt1) lstore(set0, st ^ 1, C);
+                __syncthreads();
+                st ^= 1;
+                kt = kn;
+                if (kn < kt1) kn = next_of(kn + 1, C);
+            };
+            const int full_end = min(nfull, kt1);
+            while (kt < full_end) step(std::false_type{});
+            while (kt < kt1) step(std::true_type{});
+        };
+        int kt = next_of(kt0, false);
+        if (kt < kt1) gload(set0, kt, false);
+        __builtin_amdgcn_s_waitcnt(0);
+        query_prologue();
+        if (kt < kt1) lstore(set0, st, false);
+        __syncthreads();
+        pass(std::false_type{}, kt);
+        kt = next_of(kt0, true);
+        if (kt < kt1) {
+            gload(set0, kt, true);
+            lstore(set0, st, true);
+            __syncthreads();
+        }
+        pass(std::true_type{}, kt);
+    } else {
     // Prologue: the first PF tiles' loads go out behind the query loads, and
     // one wait covers them all.
-    bool i8_c = i8_of(0), i8_n1 = i8_of(1);
     if constexpr (PF == 2) {
         gload2(set0, kt_first);
         gload2(set1, kt_first + KS);
     } else {
-        if (has(0)) gload(set0, kt_first, i8_c);
+        if (has(0)) gload(set0, kt_first, false);
     }
     __builtin_amdgcn_s_waitcnt(0);
-    if (a.neg) {
-#pragma unroll
-        for (int t = 0; t < HD / 16; ++t) qf[t] = -qf[t];
-    }
-    if constexpr (ROUTED) {
-        float sq;
-        quantize_q_regs<HD, FP8>(qf, q8, sq);
-        sq_mul = sq > 0.0f ? sq : 1.0f;   // a zero row has all-zero INT8 scores
-    }
+    query_prologue();
     if constexpr (PF == 2) lstore2(set0, 0);
-    else if (has(0)) lstore(set0, 0, i8_c);
+    else if (has(0)) lstore(set0, 0, false);
     __syncthreads();
 
-    const int kt_end = min(w_nkt, kt1);
     // One iteration; P is the parity of it (selects the staging sets).
     auto iter = [&](auto mask_tag, auto par_tag, int it) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr int P = decltype(par_tag)::value;
         const int kt = kt_first + KS * it;
-        const bool i8_cur = i8_c;
         if constexpr (PF == 2) {
             // tile it+1 is already in flight (set (it+1)%2); issue tile it+2
             // into set it%2, which tile it left at its LDS store.  Loads and
@@ -853,11 +906,9 @@ void attn_fwd_kernel(FwdArgs a) {
             if (MASK ? kt < kt_end : wave_active) tile(mask_tag, it & 1, kt, false);
             lstore2(P == 0 ? set1 : set0, (it + 1) & 1);
         } else {
-            i8_n1 = i8_of(it + 1);
-            if (has(it + 1)) gload(set0, kt + KS, i8_n1);
-            if (MASK ? kt < kt_end : wave_active) tile(mask_tag, it & 1, kt, i8_cur);
-            if (has(it + 1)) lstore(set0, (it + 1) & 1, i8_n1);
-            i8_c = i8_n1;
+            if (has(it + 1)) gload(set0, kt + KS, false);
+            if (MASK ? kt < kt_end : wave_active) tile(mask_tag, it & 1, kt, false);
+            if (has(it + 1)) lstore(set0, (it + 1) & 1, false);
         }
         __syncthreads();
     };
@@ -880,6 +931,7 @@ void attn_fwd_kernel(FwdArgs a) {
     };
     run(std::false_type{}, it_full);
     run(std::true_type{}, n_it);
+    }
 
     if constexpr (KS > 1) {
         // Merge the key groups' states into group 0 through LDS (every stage
@@ -1103,8 +1155,8 @@ hipError_t dispatch_mask(const FwdArgs& a, int grid, bool causal, bool varlen, h
 
 // Instantiated shapes: two query wavefronts with one key group for routed
 // calls with an odd head group, and with two key groups for small non-routed
-// fp16 grids; two key groups and eight query wavefronts for non-routed fp16
-// calls only; FP8 routes on fp16 inputs only.
+// fp16 grids; two key groups for non-routed fp16 calls only; eight query
+// wavefronts for fp16 K/V (routed or not); FP8 routes on fp16 inputs only.
 template <int HD>
 hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, bool varlen, bool routed,
                     bool kv8, bool fp8, hipStream_t st) {
@@ -1124,7 +1176,10 @@ hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, boo
         return dispatch_mask<HD, 4, 2, false, false>(a, grid, causal, varlen, st);
     }
     if (NW == 8) {
-        if (routed || kv8 || KS != 1) return hipErrorInvalidConfiguration;
+        if (kv8 || KS != 1) return hipErrorInvalidConfiguration;
+        if (routed)
+            return fp8 ? dispatch_mask<HD, 8, 1, true, false, true>(a, grid, causal, varlen, st)
+                       : dispatch_mask<HD, 8, 1, true, false>(a, grid, causal, varlen, st);
         return dispatch_mask<HD, 8, 1, false, false>(a, grid, causal, varlen, st);
     }
     if (routed) {
@@ -1225,14 +1280,17 @@ static Plan make_plan(const Problem& p) {
     };
     pl.combos = (varlen ? 1 : p.B) * p.n_kvh * (G / pl.HPW);
     // Workgroup shape.  A routed workgroup stays inside one 64-row query tile
-    // (two wavefronts when the head group is odd).  Unrouted fp16 calls whose
-    // grid gives two wavefronts per SIMD even so take eight query wavefronts:
-    // each K/V tile then serves twice the rows, halving the tile loads and
-    // LDS stores per FLOP.  (With fewer, four wavefronts and two key groups
-    // hide latency better than eight and a split key range.)
+    // (two wavefronts when the head group is odd).  Calls on fp16 K/V whose
+    // grid gives two wavefronts per SIMD even so take eight query wavefronts
+    // (routed ones only when the head group holds four heads, so that the
+    // eight stay inside one 64-row query tile): each K/V tile then serves
+    // twice the rows, halving the tile loads and LDS stores per FLOP.  (With
+    // fewer, four wavefronts and two key groups hide latency better than
+    // eight and a split key range.)
     pl.NW = 4;
     if (routed && pl.HPW == 1) pl.NW = 2;
-    if (!routed && !kv8 && (long long)pl.combos * blocks_of(8) * 8 >= 2 * simds) pl.NW = 8;
+    const bool nw8_ok = !kv8 && (!routed || pl.HPW == 4);
+    if (nw8_ok && (long long)pl.combos * blocks_of(8) * 8 >= 2 * simds) pl.NW = 8;
     // Small fp16 grids (under two wavefronts per SIMD) run one workgroup per
     // CU.  Under a causal mask whose diagonal spans most of the keys, the
     // workgroups of the last query rows visit every key tile and those of the
@@ -1248,9 +1306,11 @@ static Plan make_plan(const Problem& p) {
     const bool diag = p.causal && p.ksl - p.qsl < p.qsl;
     if (pl.NW == 4 && fp16_small && (diag || (long long)pl.combos * blocks_of(4) < simds / 4)) pl.NW = 2;
     const char* force_nw = getenv("ATTN_QUERY_WAVES");
-    if (!routed && !kv8 && force_nw && (force_nw[0] == '2' || force_nw[0] == '4' || force_nw[0] == '8') &&
-        force_nw[1] == 0)
-        pl.NW = force_nw[0] - '0';
+    if (force_nw && force_nw[0] && force_nw[1] == 0) {
+        const int f = force_nw[0] - '0';
+        if (!routed && !kv8 && (f == 2 || f == 4 || f == 8)) pl.NW = f;
+        if (routed && ((f == 4 && pl.HPW > 1) || (f == 8 && nw8_ok))) pl.NW = f;
+    }
     if (pl.NW == 2 && !routed && pl.HPW > 2) {
         pl.HPW = largest_div(G, 2);
         pl.combos = (varlen ? 1 : p.B) * p.n_kvh * (G / pl.HPW);

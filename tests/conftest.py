@@ -17,3 +17,13 @@ def orc():
     """The CPU fp64 oracle, built from oracle/oracle.c if no build is present."""
     import oracle
     return oracle
+
+
+@pytest.fixture(params=["auto", "nw8"])
+def routed_waves(request, monkeypatch):
+    """Workgroup shape of routed calls: what the launch plan picks for the
+    test's (small) grid, or eight query wavefronts (what large grids with a
+    four-head group get; other head groups keep their shape)."""
+    if request.param == "nw8":
+        monkeypatch.setenv("ATTN_QUERY_WAVES", "8")
+    return request.param

@@ -65,7 +65,7 @@ def test_gpu_fp8_quantizer_bitexact(A, orc, d, path):
 @pytest.mark.parametrize("heads", [(3, 3), (8, 2), (12, 3)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("tpb", [1, 3])
-def test_gpu_fp8_routed_ragged(A, orc, d, heads, causal, tpb):
+def test_gpu_fp8_routed_ragged(A, orc, d, heads, causal, tpb, routed_waves):
     rng = np.random.default_rng(1900 + d + 7 * heads[0] + heads[1] + causal + 13 * tpb)
     for (qsl, ksl) in [(1, 1), (64, 64), (130, 130), (200, 333), (300, 1000)]:
         if causal and qsl > ksl:
@@ -97,9 +97,10 @@ def test_gpu_fp8_varlen_and_all_fp8(A, orc, d, causal):
         check(got, ref)
 
 
-def test_gpu_fp8_zero_mask_is_dense_bitexact(A, monkeypatch):
+@pytest.mark.parametrize("waves", ["4", "8"])
+def test_gpu_fp8_zero_mask_is_dense_bitexact(A, monkeypatch, waves):
     monkeypatch.setenv("ATTN_KEY_GROUPS", "1")
-    monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
+    monkeypatch.setenv("ATTN_QUERY_WAVES", waves)
     rng = np.random.default_rng(1990)
     q, k, v = rand16(rng, (1, 8, 300, 128)), rand16(rng, (1, 2, 300, 128)), rand16(rng, (1, 2, 300, 128))
     zeros = W.pack_bits(np.zeros((5, 2), dtype=bool))
