@@ -1156,7 +1156,7 @@ hipError_t dispatch_mask(const FwdArgs& a, int grid, bool causal, bool varlen, h
 // Instantiated shapes: two query wavefronts with one key group for routed
 // calls with an odd head group, and with two key groups for small non-routed
 // fp16 grids; two key groups for non-routed fp16 calls only; eight query
-// wavefronts for fp16 K/V (routed or not); FP8 routes on fp16 inputs only.
+// wavefronts for every kind of call; FP8 routes on fp16 inputs only.
 template <int HD>
 hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, bool varlen, bool routed,
                     bool kv8, bool fp8, hipStream_t st) {
@@ -1176,11 +1176,13 @@ hipError_t dispatch(const FwdArgs& a, int grid, int NW, int KS, bool causal, boo
         return dispatch_mask<HD, 4, 2, false, false>(a, grid, causal, varlen, st);
     }
     if (NW == 8) {
-        if (kv8 || KS != 1) return hipErrorInvalidConfiguration;
+        if (KS != 1) return hipErrorInvalidConfiguration;
         if (routed)
             return fp8 ? dispatch_mask<HD, 8, 1, true, false, true>(a, grid, causal, varlen, st)
-                       : dispatch_mask<HD, 8, 1, true, false>(a, grid, causal, varlen, st);
-        return dispatch_mask<HD, 8, 1, false, false>(a, grid, causal, varlen, st);
+                       : kv8 ? dispatch_mask<HD, 8, 1, true, true>(a, grid, causal, varlen, st)
+                             : dispatch_mask<HD, 8, 1, true, false>(a, grid, causal, varlen, st);
+        return kv8 ? dispatch_mask<HD, 8, 1, false, true>(a, grid, causal, varlen, st)
+                   : dispatch_mask<HD, 8, 1, false, false>(a, grid, causal, varlen, st);
     }
     if (routed) {
         if (fp8) return dispatch_mask<HD, 4, 1, true, false, true>(a, grid, causal, varlen, st);
@@ -1280,16 +1282,16 @@ static Plan make_plan(const Problem& p) {
     };
     pl.combos = (varlen ? 1 : p.B) * p.n_kvh * (G / pl.HPW);
     // Workgroup shape.  A routed workgroup stays inside one 64-row query tile
-    // (two wavefronts when the head group is odd).  Calls on fp16 K/V whose
-    // grid gives two wavefronts per SIMD even so take eight query wavefronts
-    // (routed ones only when the head group holds four heads, so that the
-    // eight stay inside one 64-row query tile): each K/V tile then serves
-    // twice the rows, halving the tile loads and LDS stores per FLOP.  (With
-    // fewer, four wavefronts and two key groups hide latency better than
-    // eight and a split key range.)
+    // (two wavefronts when the head group is odd).  Calls whose grid gives
+    // two wavefronts per SIMD even so take eight query wavefronts (routed ones
+    // only when the head group holds four heads, so that the eight stay inside
+    // one 64-row query tile): each K/V tile then serves twice the rows,
+    // halving the tile loads and LDS stores per FLOP.  (With fewer, four
+    // wavefronts and two key groups hide latency better than eight and a
+    // split key range.)
     pl.NW = 4;
     if (routed && pl.HPW == 1) pl.NW = 2;
-    const bool nw8_ok = !kv8 && (!routed || pl.HPW == 4);
+    const bool nw8_ok = !routed || pl.HPW == 4;
     if (nw8_ok && (long long)pl.combos * blocks_of(8) * 8 >= 2 * simds) pl.NW = 8;
     // Small fp16 grids (under two wavefronts per SIMD) run one workgroup per
     // CU.  Under a causal mask whose diagonal spans most of the keys, the
@@ -1308,7 +1310,7 @@ static Plan make_plan(const Problem& p) {
     const char* force_nw = getenv("ATTN_QUERY_WAVES");
     if (force_nw && force_nw[0] && force_nw[1] == 0) {
         const int f = force_nw[0] - '0';
-        if (!routed && !kv8 && (f == 2 || f == 4 || f == 8)) pl.NW = f;
+        if (!routed && (f == 4 || f == 8 || (f == 2 && !kv8))) pl.NW = f;
         if (routed && ((f == 4 && pl.HPW > 1) || (f == 8 && nw8_ok))) pl.NW = f;
     }
     if (pl.NW == 2 && !routed && pl.HPW > 2) {

@@ -20,10 +20,10 @@ def orc():
 
 
 @pytest.fixture(params=["auto", "nw8"])
-def routed_waves(request, monkeypatch):
-    """Workgroup shape of routed calls: what the launch plan picks for the
-    test's (small) grid, or eight query wavefronts (what large grids with a
-    four-head group get; other head groups keep their shape)."""
+def waves8(request, monkeypatch):
+    """Workgroup shape: what the launch plan picks for the test's (small)
+    grid, or eight query wavefronts (what large grids get; routed calls only
+    with a four-head group, other head groups keep their shape)."""
     if request.param == "nw8":
         monkeypatch.setenv("ATTN_QUERY_WAVES", "8")
     return request.param

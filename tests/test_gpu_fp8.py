@@ -65,7 +65,7 @@ def test_gpu_fp8_quantizer_bitexact(A, orc, d, path):
 @pytest.mark.parametrize("heads", [(3, 3), (8, 2), (12, 3)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("tpb", [1, 3])
-def test_gpu_fp8_routed_ragged(A, orc, d, heads, causal, tpb, routed_waves):
+def test_gpu_fp8_routed_ragged(A, orc, d, heads, causal, tpb, waves8):
     rng = np.random.default_rng(1900 + d + 7 * heads[0] + heads[1] + causal + 13 * tpb)
     for (qsl, ksl) in [(1, 1), (64, 64), (130, 130), (200, 333), (300, 1000)]:
         if causal and qsl > ksl:

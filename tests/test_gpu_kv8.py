@@ -59,7 +59,7 @@ SHAPES = [(1, 1), (5, 70), (64, 64), (65, 65), (130, 130), (200, 333), (333, 200
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("heads", [(3, 3), (8, 2), (8, 1)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_gpu_kv8_dense_ragged(A, orc, d, heads, causal):
+def test_gpu_kv8_dense_ragged(A, orc, d, heads, causal, waves8):
     rng = np.random.default_rng(1200 + d + 10 * heads[0] + heads[1] + causal)
     for (qsl, ksl) in SHAPES:
         if causal and qsl > ksl:
@@ -78,7 +78,7 @@ def test_gpu_kv8_dense_ragged(A, orc, d, heads, causal):
 @pytest.mark.parametrize("heads", [(4, 2), (12, 3)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("tpb", [1, 3])
-def test_gpu_kv8_routed_ragged(A, orc, d, heads, causal, tpb):
+def test_gpu_kv8_routed_ragged(A, orc, d, heads, causal, tpb, waves8):
     rng = np.random.default_rng(1300 + d + 7 * heads[1] + causal + 13 * tpb)
     for (qsl, ksl) in [(64, 64), (130, 130), (200, 333), (300, 1000)]:
         if causal and qsl > ksl:
@@ -95,7 +95,7 @@ def test_gpu_kv8_routed_ragged(A, orc, d, heads, causal, tpb):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("routed", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
-def test_gpu_kv8_varlen_ragged(A, orc, d, routed, causal):
+def test_gpu_kv8_varlen_ragged(A, orc, d, routed, causal, waves8):
     rng = np.random.default_rng(1400 + d + routed + 2 * causal)
     lens = [1, 63, 64, 65, 200, 0, 130, 7]
     cu = W.cu_seqlens_of(lens)

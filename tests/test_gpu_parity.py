@@ -122,13 +122,13 @@ def test_varlen_ragged(A, orc, d, heads, causal, key_groups):
 @pytest.mark.parametrize("heads", [(2, 2), (4, 2), (8, 2), (12, 3)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("tpb", [1, 3, 4])
-def test_routed_ragged(A, orc, d, heads, causal, tpb, routed_waves):
+def test_routed_ragged(A, orc, d, heads, causal, tpb, waves8):
     rng = np.random.default_rng(3 * d + heads[0] + 5 * heads[1] + causal + 11 * tpb)
     for (qsl, ksl) in [(64, 64), (130, 130), (200, 700), (333, 200)]:
         if causal and qsl > ksl:
             continue
         say("routed d=%d heads=%s causal=%d tpb=%d qsl=%d ksl=%d shape=%s" % (d, heads, causal, tpb, qsl, ksl,
-                                                                           routed_waves))
+                                                                           waves8))
         q, k, v = rand16(rng, (1, heads[0], qsl, d)), rand16(rng, (1, heads[1], ksl, d)), \
             rand16(rng, (1, heads[1], ksl, d))
         route = W.draw_route(qsl, ksl, tpb, 0.5, seed=int(rng.integers(1 << 30)))
@@ -142,7 +142,7 @@ def test_routed_ragged(A, orc, d, heads, causal, tpb, routed_waves):
 @pytest.mark.parametrize("heads", [(2, 2), (8, 2)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("tpb", [1, 3, 4])
-def test_routed_varlen_ragged(A, orc, d, heads, causal, tpb, routed_waves):
+def test_routed_varlen_ragged(A, orc, d, heads, causal, tpb, waves8):
     """Packed batch with a bitmask: every sequence reads its own stacked rows."""
     rng = np.random.default_rng(500 + d + 7 * heads[1] + causal + 13 * tpb)
     lens = [1, 63, 64, 65, 200, 0, 130, 7]
@@ -151,7 +151,7 @@ def test_routed_varlen_ragged(A, orc, d, heads, causal, tpb, routed_waves):
     n_rows = sum(-(-L // 64) for L in lens)
     n_g = W.n_route_groups(T, tpb)
     route = W.pack_bits(rng.random((n_rows, n_g)) < 0.5)
-    say("routed varlen d=%d heads=%s causal=%d tpb=%d shape=%s" % (d, heads, causal, tpb, routed_waves))
+    say("routed varlen d=%d heads=%s causal=%d tpb=%d shape=%s" % (d, heads, causal, tpb, waves8))
     q, k, v = rand16(rng, (heads[0], T, d)), rand16(rng, (heads[1], T, d)), rand16(rng, (heads[1], T, d))
     got = gpu_attn(A, q, k, v, 0.1, causal, cu=cu, route=route, tpb=tpb)
     ref = orc.attn_fwd(q, k, v, scale=0.1, causal=causal, cu_seqlens=cu, route=route, tiles_per_bit=tpb)
