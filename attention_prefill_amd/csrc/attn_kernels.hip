@@ -813,11 +813,6 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int t = 0; t < HD / 16; ++t) qf[t] = -qf[t];
         }
-        if constexpr (ROUTED) {
-            float sq;
-            quantize_q_regs<HD, FP8>(qf, q8, sq);
-            sq_mul = sq > 0.0f ? sq : 1.0f;   // a zero row has all-zero INT8 scores
-        }
     };
     if constexpr (ROUTED) {
         // Routed calls take their tiles in two passes, first every FP16 tile
@@ -872,10 +867,15 @@ void attn_fwd_kernel(FwdArgs a) {
         kt = next_of(kt0, true);
         if (kt < kt1) {
             gload(set0, kt, true);
+            // the query codes are made here, so that they are not live
+            // through the FP16 pass
+            float sq;
+            quantize_q_regs<HD, FP8>(qf, q8, sq);
+            sq_mul = sq > 0.0f ? sq : 1.0f;   // a zero row has all-zero INT8 scores
             lstore(set0, st, true);
             __syncthreads();
+            pass(std::true_type{}, kt);
         }
-        pass(std::true_type{}, kt);
     } else {
     // Prologue: the first PF tiles' loads go out behind the query loads, and
     // one wait covers them all.
