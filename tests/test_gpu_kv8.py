@@ -130,15 +130,19 @@ def test_gpu_kv8_all_int8_and_zero_rows(A, orc):
         check(got, ref)
 
 
-def test_gpu_kv8_split_keys(A, orc, monkeypatch):
-    """Key range split over workgroups (partials and merge) on the cache path."""
-    rng = np.random.default_rng(1600)
+@pytest.mark.parametrize("routed", [False, True])
+def test_gpu_kv8_split_keys(A, orc, monkeypatch, routed):
+    """Key range split over workgroups (partials and merge) on the cache path,
+    with and without a bitmask (routed splits walk each route's tiles from
+    their own start)."""
+    rng = np.random.default_rng(1600 + routed)
     q = rand16(rng, (1, 8, 100, 128))
     k8, sk, v8, sv = encode(orc, rand16(rng, (1, 2, 2000, 128)), rand16(rng, (1, 2, 2000, 128)))
-    ref = orc.attn_fwd_kv8(q, k8, sk, v8, sv, scale=0.1, causal=True)
-    for ks in ("1", "3"):
+    route = W.pack_bits(rng.random((2, W.n_route_groups(2000, 1))) < 0.5) if routed else None
+    ref = orc.attn_fwd_kv8(q, k8, sk, v8, sv, scale=0.1, causal=True, route=route, tiles_per_bit=1)
+    for ks in ("1", "3", "4"):
         monkeypatch.setenv("ATTN_KSPLIT", ks)
-        check(gpu_kv8(A, q, k8, sk, v8, sv, 0.1, True), ref, ks)
+        check(gpu_kv8(A, q, k8, sk, v8, sv, 0.1, True, route=route, tpb=1), ref, ks)
 
 
 @pytest.mark.parametrize("name", [n for n, w in W.WORKLOADS.items() if w.kv8])

@@ -158,6 +158,29 @@ def test_routed_varlen_ragged(A, orc, d, heads, causal, tpb, waves8):
     check(got, ref)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tpb", [1, 3])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lowp", ["int8", "fp8"])
+@pytest.mark.parametrize("ks", ["2", "3", "5"])
+def test_gpu_routed_split_keys(A, orc, monkeypatch, d, tpb, causal, lowp, ks, waves8):
+    """Key range split over workgroups on routed calls: every split walks its
+    own tiles of each route (FP16 pass, then low-precision pass) from a start
+    that may fall inside a routing group and inside a bitmask word (40 tiles,
+    up to 40 groups, two words per row)."""
+    rng = np.random.default_rng(4000 + d + 7 * tpb + causal + 3 * int(ks) + (lowp == "fp8"))
+    qsl, ksl = 100, 2500
+    q, k, v = rand16(rng, (1, 8, qsl, d)), rand16(rng, (1, 2, ksl, d)), rand16(rng, (1, 2, ksl, d))
+    route = W.pack_bits(rng.random((-(-qsl // 64), W.n_route_groups(ksl, tpb))) < 0.5)
+    monkeypatch.setenv("ATTN_KSPLIT", ks)
+    say("routed split d=%d tpb=%d causal=%d lowp=%s splits=%s shape=%s" % (d, tpb, causal, lowp, ks, waves8))
+    got = A.attn_fwd(dev(q), dev(k), dev(v), scale=0.1, causal=causal, route_bitmask=words_tensor(route),
+                     tiles_per_bit=tpb, lowp=lowp)
+    torch.cuda.synchronize()
+    ref = orc.attn_fwd(q, k, v, scale=0.1, causal=causal, route=route, tiles_per_bit=tpb, lowp=lowp)
+    check(got.cpu().numpy(), ref, (lowp, ks))
+
+
 @pytest.mark.parametrize("waves", ["4", "8"])
 def test_gpu_routed_varlen_zero_mask_is_dense(A, monkeypatch, waves):
     """Routed calls run one key group; both calls are pinned to the same
