@@ -8,11 +8,14 @@ synthetic input (for the default workload: one non-causal and one causal
 call on the same Q/K/V).  Inputs are resident in HBM before the timed
 region starts.  The value is the throughput convention of the "Nax Refactor"
 timing tables (ml-explore/mlx pull request 3271): 4*B*n_qh*qsl*ksl*hdim FLOP
-per call, halved when causal, divided by wall time.
+per call, halved when causal, divided by wall time.  Before the W warmup
+steps, untimed steps run for about one second (--settle-ms), so that the GPU
+clock has left its idle level before anything is timed.
 
 Printed: one JSON line with the metric, a roofline record of the dominant
-kernel (its per-launch time measured with HIP events on its own stream) and
-the CPU oracle's throughput on a bounded sample of the same workload.
+kernel (its per-launch time measured with HIP events on its own stream, in a
+second pass over the same steps, since event records cost GPU time of their
+own) and the CPU oracle's throughput on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -57,6 +60,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
+                    help="before the warmup steps, run untimed steps until this much wall time has "
+                         "passed, so that the GPU clock has reached its sustained level (0: none)")
     ap.add_argument("--workload", default="dense_1024_d64_pair", choices=sorted(BENCH_SETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fp16-compare", action="store_true",
@@ -218,16 +224,38 @@ def main():
         for c in calls:
             c(stream)
 
+    # the GPU raises its clock only after tens of milliseconds of sustained
+    # work: without this, short workloads are timed partly at idle clocks
+    settle_steps = 0
+    ts = time.perf_counter()
+    while (time.perf_counter() - ts) * 1e3 < args.settle_ms:
+        step()
+        torch.cuda.synchronize()
+        settle_steps += 1
+    settle_ms = (time.perf_counter() - ts) * 1e3
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # dominant kernel: the call with the most FLOP; HIP events on its stream
+    # the timed steps: calls only
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_per_step = (t1 - t0) / args.steps
+
+    # the dominant kernel (the call with the most FLOP): the same steps again,
+    # with HIP events recorded around that kernel on its stream.  An event
+    # record is a timestamped barrier packet that costs GPU time of its own,
+    # so the throughput above is timed without them.
     dom = max(range(len(calls)), key=lambda i: calls[i].visited_flop)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    te0 = time.perf_counter()
     for s in range(args.steps):
         for i, c in enumerate(calls):
             if i == dom:
@@ -236,9 +264,8 @@ def main():
             if i == dom:
                 ev[s][1].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    te1 = time.perf_counter()
 
-    sec_per_step = (t1 - t0) / args.steps
     metric_flop = sum(c.metric_flop for c in calls)
     value = metric_flop / sec_per_step / 1e12
     dom_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
@@ -253,7 +280,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / FP16_PEAK_TFLOPS, 4),
                 "traffic": hbm_traffic(args.workload, dom_name), "kernel": dom_name,
-                "flop_per_launch": dc.visited_flop, "avg_launch_ms": round(dom_ms, 5)}
+                "flop_per_launch": dc.visited_flop, "avg_launch_ms": round(dom_ms, 5),
+                "ms_per_step_with_events": round((te1 - te0) / args.steps * 1e3, 5)}
 
     # the page's figures for the same shapes, combined like the value
     page = []
@@ -274,7 +302,8 @@ def main():
            "low_precision_route": w0.lowp if w0.tiles_per_bit else None,
            "calls_per_step": len(calls)}
     rec = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec_per_step * 1e3, 5),
+           "steps": args.steps, "warmup": args.warmup, "settle_steps": settle_steps,
+           "settle_ms": round(settle_ms, 1), "ms_per_step": round(sec_per_step * 1e3, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": vs, "dtype": "fp16",
            "data": "synthetic: i.i.d. N(0,1) Q/K/V cast to fp16 (numpy default_rng, seeded)" +
                    ("; K and V as an INT8 key/value cache encoded on the device"
