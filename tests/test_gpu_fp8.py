@@ -81,7 +81,7 @@ def test_gpu_fp8_routed_ragged(A, orc, d, heads, causal, tpb, waves8):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_gpu_fp8_varlen_and_all_fp8(A, orc, d, causal):
+def test_gpu_fp8_varlen_and_all_fp8(A, orc, d, causal, waves8):
     rng = np.random.default_rng(1950 + d + causal)
     lens = [1, 63, 64, 65, 200, 0, 130, 7]
     cu = W.cu_seqlens_of(lens)

@@ -158,6 +158,26 @@ def test_routed_varlen_ragged(A, orc, d, heads, causal, tpb, waves8):
     check(got, ref)
 
 
+@pytest.mark.parametrize("shape", ["nw2", "kg2", "nw8"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("ks", ["2", "3"])
+def test_gpu_dense_split_keys_all_shapes(A, orc, monkeypatch, shape, causal, ks):
+    """Key range split over workgroups (fp32 partials and the merge kernel)
+    under every non-routed workgroup shape, at hdim 64 with a head group of 2."""
+    rng = np.random.default_rng(4500 + 3 * int(ks) + causal + 10 * ["nw2", "kg2", "nw8"].index(shape))
+    q, k, v = rand16(rng, (1, 4, 200, 64)), rand16(rng, (1, 2, 2100, 64)), rand16(rng, (1, 2, 2100, 64))
+    if shape == "kg2":
+        monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
+        monkeypatch.setenv("ATTN_KEY_GROUPS", "2")
+    else:
+        monkeypatch.setenv("ATTN_QUERY_WAVES", shape[2])
+    monkeypatch.setenv("ATTN_KSPLIT", ks)
+    say("dense split shape=%s causal=%d splits=%s" % (shape, causal, ks))
+    got = gpu_attn(A, q, k, v, 0.125, causal)
+    ref = orc.attn_fwd(q, k, v, scale=0.125, causal=causal)
+    check(got, ref, (shape, ks))
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("tpb", [1, 3])
 @pytest.mark.parametrize("causal", [False, True])
@@ -212,15 +232,21 @@ def test_routed_all_int8(A, orc, d):
         check(got, ref)
 
 
-def test_negative_scale(A, orc):
-    rng = np.random.default_rng(50)
-    q, k, v = rand16(rng, (1, 4, 100, 64)), rand16(rng, (1, 2, 150, 64)), rand16(rng, (1, 2, 150, 64))
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("lowp", ["int8", "fp8"])
+def test_negative_scale(A, orc, d, lowp, waves8):
+    """A negative scale (the queries are negated in the prologue, before any
+    low-precision codes are made), dense and routed, both workgroup shapes."""
+    rng = np.random.default_rng(50 + d + (lowp == "fp8"))
+    q, k, v = rand16(rng, (1, 8, 100, d)), rand16(rng, (1, 2, 150, d)), rand16(rng, (1, 2, 150, d))
     route = W.pack_bits(rng.random((2, 3)) < 0.5)
-    say("negative scale")
+    say("negative scale d=%d lowp=%s shape=%s" % (d, lowp, waves8))
     for r in (None, route):
-        got = gpu_attn(A, q, k, v, -0.125, True, route=r, tpb=1)
-        ref = orc.attn_fwd(q, k, v, scale=-0.125, causal=True, route=r, tiles_per_bit=1)
-        check(got, ref)
+        got = A.attn_fwd(dev(q), dev(k), dev(v), scale=-0.125, causal=True, route_bitmask=words_tensor(r),
+                         tiles_per_bit=1, lowp=lowp)
+        torch.cuda.synchronize()
+        ref = orc.attn_fwd(q, k, v, scale=-0.125, causal=True, route=r, tiles_per_bit=1, lowp=lowp)
+        check(got.cpu().numpy(), ref)
 
 
 # --------------------------------------------------------------------------
