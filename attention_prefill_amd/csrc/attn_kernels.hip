@@ -253,6 +253,8 @@ struct FwdArgs {
     int tiles_per_bit, wpr;
     float c;                // |scale| * log2(e)
     int neg;                // scale < 0: queries are negated
+    int pair_blocks;        // causal, whole grid resident: the second half of the
+                            // row blocks runs light-first (see make_plan)
     int ksplit;             // key-range splits per query block (1: write out directly)
     float* part_o;          // split partials: [ksplit, rows, HD] O / l (fp32)
     float* part_l;          // and [ksplit, rows] log2 of the softmax denominator, base-2 units
@@ -337,7 +339,8 @@ void attn_fwd_kernel(FwdArgs a) {
         }
     } else {
         const int b = combo / (hpc * a.n_kvh);
-        mb = CAUSAL ? (a.n_mblk - 1 - rank) : rank;
+        const int half = a.n_mblk / 2;
+        mb = !CAUSAL ? rank : (a.pair_blocks && rank >= half) ? rank - half : a.n_mblk - 1 - rank;
         Lq = a.qsl;
         Lk = a.ksl;
         qrow0 = ((size_t)b * a.n_qh + h) * Lq;
@@ -1252,6 +1255,7 @@ static int largest_div(int G, int cap) {
 // Launch plan of one forward call: workgroup shape, key splits, scratch layout.
 struct Plan {
     int NW, KS, HPW, BM, combos, n_mblk, ksplit;
+    int pair_blocks;
     long long grid;
     size_t k8_off, sk_off, po_off, pl_off, bytes;   // scratch layout (bytes)
     long long out_rows;
@@ -1336,6 +1340,16 @@ static Plan make_plan(const Problem& p) {
     if (force && force[0] >= '1' && force[0] <= '8' && force[1] == 0) ks = force[0] - '0';
     pl.ksplit = ks;
     pl.grid = (long long)pl.combos * pl.ksplit * pl.n_mblk;
+    // Causal row blocks run heavy-first.  When every workgroup of the grid is
+    // resident at once, two to a CU (two-wavefront workgroups), workgroups i
+    // and i + grid/2 share a CU; the second half then runs light-first, so
+    // the heaviest block shares its CU with the lightest one and every CU
+    // gets about the same number of key tiles.
+    pl.pair_blocks = (p.causal && !varlen && pl.NW == 2 && pl.KS == 2 && !routed && pl.ksplit == 1 &&
+                      pl.grid == 2LL * cu_count() && pl.n_mblk % 2 == 0) ? 1 : 0;
+    const char* force_pair = getenv("ATTN_PAIR_BLOCKS");
+    if (force_pair && (force_pair[0] == '0' || force_pair[0] == '1') && force_pair[1] == 0)
+        pl.pair_blocks = (force_pair[0] == '1' && p.causal && !varlen) ? 1 : 0;
     pl.out_rows = varlen ? (long long)p.n_qh * p.qsl : (long long)p.B * p.n_qh * p.qsl;
     size_t off = 0;
     if (routed && !kv8) {
@@ -1382,6 +1396,7 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
     a.HPW = pl.HPW;
     a.combos = pl.combos;
     a.n_mblk = pl.n_mblk;
+    a.pair_blocks = pl.pair_blocks;
     a.ksplit = pl.ksplit;
     a.part_rows = pl.out_rows;
     a.part_o = pl.ksplit > 1 ? (float*)((char*)scratch + pl.po_off) : nullptr;

@@ -159,6 +159,27 @@ def test_routed_varlen_ragged(A, orc, d, heads, causal, tpb, waves8):
 
 
 @pytest.mark.parametrize("shape", ["nw2", "kg2", "nw8"])
+@pytest.mark.parametrize("qsl", [64, 200, 448, 1000])
+def test_gpu_causal_paired_block_order(A, orc, monkeypatch, shape, qsl):
+    """Causal row blocks with the second half of the grid run light-first
+    (what a fully resident grid of two-wavefront workgroups gets): every row
+    is computed once, for even and odd block counts and every shape."""
+    rng = np.random.default_rng(4700 + qsl + 7 * ["nw2", "kg2", "nw8"].index(shape))
+    q, k, v = rand16(rng, (1, 8, qsl, 64)), rand16(rng, (1, 4, qsl + 37, 64)), rand16(rng, (1, 4, qsl + 37, 64))
+    if shape == "kg2":
+        monkeypatch.setenv("ATTN_QUERY_WAVES", "4")
+        monkeypatch.setenv("ATTN_KEY_GROUPS", "2")
+    else:
+        monkeypatch.setenv("ATTN_QUERY_WAVES", shape[2])
+    monkeypatch.setenv("ATTN_KSPLIT", "1")
+    monkeypatch.setenv("ATTN_PAIR_BLOCKS", "1")
+    say("paired blocks shape=%s qsl=%d" % (shape, qsl))
+    got = gpu_attn(A, q, k, v, 0.125, True)
+    ref = orc.attn_fwd(q, k, v, scale=0.125, causal=True)
+    check(got, ref, (shape, qsl))
+
+
+@pytest.mark.parametrize("shape", ["nw2", "kg2", "nw8"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("ks", ["2", "3"])
 def test_gpu_dense_split_keys_all_shapes(A, orc, monkeypatch, shape, causal, ks):
