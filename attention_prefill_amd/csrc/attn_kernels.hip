@@ -74,6 +74,9 @@ constexpr int TQ = 64;          // query rows per routing tile
 constexpr int BN = ATTN_KEY_TILE;   // keys per kernel tile (64 or 32)
 static_assert(BN == 64 || BN == 32, "key tile must be 64 or 32");
 constexpr int NKB = BN / 32;        // 32-key score blocks per tile
+#ifndef ATTN_STAGES4
+#define ATTN_STAGES4 1
+#endif
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23
 // dword 3 of a raw buffer descriptor (32-bit data format, no swizzle, no
@@ -222,6 +225,13 @@ __device__ __forceinline__ bool route_bit(const uint32_t* row, int kt, int tiles
 // and INT8 key/value caches).  Row pitches are padded so that the
 // row-parallel operand reads and the staging writes spread over the banks.
 // ---------------------------------------------------------------------------
+// LDS stages of a kernel shape: the eight-wavefront kernels keep four
+// (tiles are stored two ahead, so one barrier covers two tiles); the others
+// two.
+__host__ __device__ constexpr int n_stages(int nw, int ks, bool routed) {
+    return (ATTN_STAGES4 && nw == 8 && ks == 1) ? 4 : 2;
+}
+
 template <int HD>
 struct Lds {
     static constexpr int KP = HD + 8;            // fp16 elements per K row
@@ -287,6 +297,8 @@ void attn_fwd_kernel(FwdArgs a) {
     // Tiles in flight ahead of the one computed.  Two need a second staging
     // set, which only the hdim-64 FP16 kernel has registers for.
     constexpr int PF = (HD == 64 && !ROUTED && !KV8 && NW == 4 && BN == 64) ? 2 : 1;
+    // four LDS stages and tiles stored two ahead: a barrier every other tile
+    constexpr int NST = n_stages(NW, KS, ROUTED);
     // Request all of a tile's K and V fragments before its first MFMA (the
     // hdim-64 kernel has the registers for them).
     constexpr bool EARLY = (HD == 64);
@@ -842,40 +854,77 @@ void attn_fwd_kernel(FwdArgs a) {
             return kt1;
         };
         int st = 0;
-        // tiles [kt, kt1) of route C, the first (kt) already in LDS stage st
+        // tiles [kt, kt1) of route C: the first (kt) already in LDS stage st
+        // and, with four stages, the second in stage st+1; with four stages
+        // tiles are stored two ahead and a barrier follows every other step
+        // (and the end of the pass, after which the next pass may store into
+        // any stage)
         auto pass = [&](auto cls_tag, int kt) __attribute__((always_inline)) {
             constexpr bool C = decltype(cls_tag)::value;
             int kn = next_of(kt + 1, C);
+            int kn2 = (NST == 4 && kn < kt1) ? next_of(kn + 1, C) : kt1;
+            int si = 0;
             auto step = [&](auto mask_tag) __attribute__((always_inline)) {
                 constexpr bool MASK = decltype(mask_tag)::value;
-                if (kn < kt1) gload(set0, kn, C);
-                if (MASK ? kt < kt_end : wave_active) tile(mask_tag, st, kt, C);
-                if (kn < kt1) lstore(set0, st ^ 1, C);
-                __syncthreads();
-                st ^= 1;
-                kt = kn;
-                if (kn < kt1) kn = next_of(kn + 1, C);
+                if constexpr (NST == 4) {
+                    if (kn2 < kt1) gload(set0, kn2, C);
+                    if (MASK ? kt < kt_end : wave_active) tile(mask_tag, st, kt, C);
+                    if (kn2 < kt1) lstore(set0, (st + 2) & 3, C);
+                    if (si & 1) __syncthreads();
+                    ++si;
+                    st = (st + 1) & 3;
+                    kt = kn;
+                    kn = kn2;
+                    if (kn2 < kt1) kn2 = next_of(kn2 + 1, C);
+                } else {
+                    if (kn < kt1) gload(set0, kn, C);
+                    if (MASK ? kt < kt_end : wave_active) tile(mask_tag, st, kt, C);
+                    if (kn < kt1) lstore(set0, st ^ 1, C);
+                    __syncthreads();
+                    st ^= 1;
+                    kt = kn;
+                    if (kn < kt1) kn = next_of(kn + 1, C);
+                }
             };
             const int full_end = min(nfull, kt1);
             while (kt < full_end) step(std::false_type{});
             while (kt < kt1) step(std::true_type{});
+            if constexpr (NST == 4) __syncthreads();
         };
-        int kt = next_of(kt0, false);
+        // first two tiles of route c from kt0 (the second is kt1 with two stages)
+        auto first2 = [&](bool c, int& t0, int& t1) __attribute__((always_inline)) {
+            t0 = next_of(kt0, c);
+            t1 = (NST == 4 && t0 < kt1) ? next_of(t0 + 1, c) : kt1;
+        };
+        int kt, kt2;
+        first2(false, kt, kt2);
         if (kt < kt1) gload(set0, kt, false);
+        if constexpr (NST == 4) {
+            if (kt2 < kt1) gload(set1, kt2, false);
+        }
         __builtin_amdgcn_s_waitcnt(0);
         query_prologue();
         if (kt < kt1) lstore(set0, st, false);
+        if constexpr (NST == 4) {
+            if (kt2 < kt1) lstore(set1, (st + 1) & 3, false);
+        }
         __syncthreads();
         pass(std::false_type{}, kt);
-        kt = next_of(kt0, true);
+        first2(true, kt, kt2);
         if (kt < kt1) {
             gload(set0, kt, true);
+            if constexpr (NST == 4) {
+                if (kt2 < kt1) gload(set1, kt2, true);
+            }
             // the query codes are made here, so that they are not live
             // through the FP16 pass
             float sq;
             quantize_q_regs<HD, FP8>(qf, q8, sq);
             sq_mul = sq > 0.0f ? sq : 1.0f;   // a zero row has all-zero INT8 scores
             lstore(set0, st, true);
+            if constexpr (NST == 4) {
+                if (kt2 < kt1) lstore(set1, (st + 1) & 3, true);
+            }
             __syncthreads();
             pass(std::true_type{}, kt);
         }
@@ -887,11 +936,17 @@ void attn_fwd_kernel(FwdArgs a) {
         gload2(set1, kt_first + KS);
     } else {
         if (has(0)) gload(set0, kt_first, false);
+        if constexpr (NST == 4) {
+            if (has(1)) gload(set1, kt_first + KS, false);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0);
     query_prologue();
     if constexpr (PF == 2) lstore2(set0, 0);
     else if (has(0)) lstore(set0, 0, false);
+    if constexpr (NST == 4) {
+        if (has(1)) lstore(set1, 1, false);
+    }
     __syncthreads();
 
     // One iteration; P is the parity of it (selects the staging sets).
@@ -908,6 +963,15 @@ void attn_fwd_kernel(FwdArgs a) {
             gload2(P == 0 ? set0 : set1, kt + 2 * KS);
             if (MASK ? kt < kt_end : wave_active) tile(mask_tag, it & 1, kt, false);
             lstore2(P == 0 ? set1 : set0, (it + 1) & 1);
+        } else if constexpr (NST == 4) {
+            // tile it+2 goes to stage (it+2)%4, last read in iteration it-2;
+            // a barrier after every odd iteration separates each store from
+            // its reads and each read from the next store into its stage
+            if (has(it + 2)) gload(set0, kt + 2 * KS, false);
+            if (MASK ? kt < kt_end : wave_active) tile(mask_tag, it & 3, kt, false);
+            if (has(it + 2)) lstore(set0, (it + 2) & 3, false);
+            if (it & 1) __syncthreads();
+            return;
         } else {
             if (has(it + 1)) gload(set0, kt + KS, false);
             if (MASK ? kt < kt_end : wave_active) tile(mask_tag, it & 1, kt, false);
@@ -1140,7 +1204,7 @@ hipError_t set_lds(K kernel, int bytes) {
 template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8, bool FP8>
 hipError_t launch_fwd_t(const FwdArgs& a, int grid, hipStream_t st) {
     auto kern = attn_fwd_kernel<HD, NW, KS, CAUSAL, VARLEN, ROUTED, KV8, FP8>;
-    constexpr int lds = Lds<HD>::TOTAL * KS;
+    constexpr int lds = Lds<HD>::STAGE * n_stages(NW, KS, ROUTED) * KS;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * KS * 64), lds, st, a);
