@@ -94,3 +94,22 @@ def test_gpu_many_short_sequences(A, orc, routed):
     torch.cuda.synchronize()
     ref = orc.attn_fwd(q, k, v, scale=0.125, causal=True, cu_seqlens=cu, route=route, tiles_per_bit=1)
     check(got.cpu().numpy(), ref, "many")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("qsl", [1, 7])
+@pytest.mark.parametrize("routed", [False, True])
+def test_gpu_few_queries_long_keys(A, orc, d, qsl, routed):
+    """A few query rows against 70000 keys (bottom-right causal: every row
+    sees nearly all of them): the key range is split over the most
+    workgroups and merged; full oracle."""
+    rng = np.random.default_rng(5000 + d + qsl + 3 * routed)
+    L = 70000
+    say("few queries: qsl=%d ksl=%d d=%d routed=%d" % (qsl, L, d, routed))
+    q, k, v = rand16(rng, (1, 8, qsl, d)), rand16(rng, (1, 2, L, d)), rand16(rng, (1, 2, L, d))
+    route = W.pack_bits(rng.random((1, W.n_route_groups(L, 2))) < 0.5) if routed else None
+    got = A.attn_fwd(dev(q), dev(k), dev(v), scale=0.1, causal=True, route_bitmask=words_tensor(route),
+                     tiles_per_bit=2)
+    torch.cuda.synchronize()
+    ref = orc.attn_fwd(q, k, v, scale=0.1, causal=True, route=route, tiles_per_bit=2)
+    check(got.cpu().numpy(), ref, (qsl, d, routed))
