@@ -60,6 +60,8 @@ def load():
         lib.attn_fwd_lowp_stream.restype = _I
         lib.attn_fwd_unfused_stream.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]
         lib.attn_fwd_unfused_stream.restype = _I
+        lib.attn_debug_plan.argtypes = [_I] * 9 + [ctypes.POINTER(ctypes.c_int64)]
+        lib.attn_debug_plan.restype = _I
         _lib = lib
     return _lib
 
@@ -267,3 +269,17 @@ def attn_fwd_unfused(q, k, v, out=None, *, scale=None, causal=False, stream=None
     _check(load().attn_fwd_unfused_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, qsl, ksl, d, n_qh, n_kvh,
                                           float(scale), int(bool(causal)), _stream(stream)))
     return out
+
+
+PLAN_FIELDS = ("query_waves", "key_groups", "heads_per_wg", "rows_per_wg", "columns", "row_blocks",
+               "key_splits", "pair_blocks", "grid", "scratch_bytes")
+
+
+def attn_debug_plan(B, qsl, ksl, hdim, n_qh, n_kvh, causal, tiles_per_bit=4, *, packed=False, routed=False,
+                    kv8=False, fp8=False):
+    """The launch plan the forward entry points would use for these sizes
+    (test hook; no device needed): a dict of PLAN_FIELDS."""
+    out = (ctypes.c_int64 * 10)()
+    flags = int(bool(packed)) | (int(bool(routed)) << 1) | (int(bool(kv8)) << 2) | (int(bool(fp8)) << 3)
+    _check(load().attn_debug_plan(B, qsl, ksl, hdim, n_qh, n_kvh, int(bool(causal)), int(tiles_per_bit), flags, out))
+    return dict(zip(PLAN_FIELDS, (int(x) for x in out)))

@@ -230,6 +230,31 @@ attn_status attn_debug_quantize_rows(const void* x_f16, int32_t rows, int32_t hd
     return quantize_rows(x_f16, (long long)rows, hdim, q8, scale_out, path, (hipStream_t)hip_stream);
 }
 
+attn_status attn_debug_plan(int32_t B, int32_t qsl, int32_t ksl, int32_t hdim, int32_t n_qh, int32_t n_kvh,
+                            int32_t causal, int32_t tiles_per_bit, int32_t flags, int64_t* plan_out) {
+    if (!plan_out) return fail(ATTN_ERR_NULL, "plan_out must be a non-null host pointer");
+    if (flags & ~15) return fail(ATTN_ERR_ARG, "flags has unknown bits (0x%x)", (unsigned)flags);
+    // stand-in device addresses: validated for alignment, never read
+    char* const fake = reinterpret_cast<char*>(uintptr_t(1) << 20);
+    attn::Problem p{fake, fake, fake, fake, B, qsl, ksl, hdim, n_qh, n_kvh, 1.0f, causal != 0,
+                    (flags & 1) ? reinterpret_cast<const int32_t*>(fake) : nullptr,
+                    (flags & 2) ? reinterpret_cast<const uint32_t*>(fake) : nullptr, tiles_per_bit};
+    if (flags & 4) {
+        p.k8 = reinterpret_cast<const int8_t*>(fake);
+        p.v8 = reinterpret_cast<const int8_t*>(fake);
+        p.k_scale = reinterpret_cast<const float*>(fake);
+        p.v_scale = reinterpret_cast<const float*>(fake);
+    }
+    if (flags & 8) p.lowp = ATTN_LOWP_FP8_E4M3;
+    attn_status vs = validate(p);
+    if (vs != ATTN_OK) return vs;
+    long long out[10];
+    attn::forward_plan(p, out);
+    for (int i = 0; i < 10; ++i) plan_out[i] = out[i];
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
 attn_status attn_debug_route_dump(const uint32_t* route_bitmask, int32_t qsl, int32_t ksl,
                                   int32_t causal, int32_t tiles_per_bit, uint8_t* route_out,
                                   void* hip_stream) {

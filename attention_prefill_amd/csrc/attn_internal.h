@@ -31,6 +31,11 @@ struct Problem {
 // Device scratch a forward call needs (bytes): quantised K rows for routed
 // calls and split-key partials when the key range is split.  0 if none.
 size_t forward_scratch_bytes(const Problem& p);
+// The launch plan of a forward call (no device access): query wavefronts per
+// workgroup, key groups, heads per workgroup, rows per workgroup, workgroup
+// columns, row blocks per column, key splits, light-first pairing, grid size,
+// scratch bytes.
+void forward_plan(const Problem& p, long long out[10]);
 
 // Enqueue the whole forward pass on stream.  scratch must hold
 // forward_scratch_bytes(p) bytes (may be null when that is 0).

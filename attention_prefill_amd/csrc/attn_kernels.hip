@@ -1435,6 +1435,20 @@ static Plan make_plan(const Problem& p) {
 
 size_t forward_scratch_bytes(const Problem& p) { return make_plan(p).bytes; }
 
+void forward_plan(const Problem& p, long long out[10]) {
+    const Plan pl = make_plan(p);
+    out[0] = pl.NW;
+    out[1] = pl.KS;
+    out[2] = pl.HPW;
+    out[3] = pl.BM;
+    out[4] = pl.combos;
+    out[5] = pl.n_mblk;
+    out[6] = pl.ksplit;
+    out[7] = pl.pair_blocks;
+    out[8] = pl.grid;
+    out[9] = (long long)pl.bytes;
+}
+
 hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
     const Plan pl = make_plan(p);
     FwdArgs a;

@@ -194,6 +194,21 @@ attn_status attn_debug_route_dump(const uint32_t* route_bitmask, int32_t qsl, in
                                   int32_t causal, int32_t tiles_per_bit, uint8_t* route_out,
                                   void* hip_stream);
 
+/* Test hook for the launch planner: the workgroup shape and grid that the
+ * forward entry points would launch for these sizes.  Nothing is launched and
+ * no device memory is touched.  flags: bit 0 packed batch (cu_seqlens set,
+ * qsl == ksl == total tokens, B sequences), bit 1 routed (route_bitmask set),
+ * bit 2 INT8 key/value cache, bit 3 FP8 route; other bits are ATTN_ERR_ARG.
+ * The sizes are validated as for attn_fwd (scale taken as 1).  plan_out: host
+ * int64[10], filled on ATTN_OK with: query wavefronts per workgroup, key
+ * groups per workgroup, query heads per workgroup, query rows per workgroup,
+ * workgroup columns, row blocks per column, key splits, 1 if the second half
+ * of the causal row blocks runs light-first, grid size, scratch bytes.  The
+ * plan uses the current device's CU count, or 256 when no device is
+ * visible. */
+attn_status attn_debug_plan(int32_t B, int32_t qsl, int32_t ksl, int32_t hdim, int32_t n_qh, int32_t n_kvh,
+                            int32_t causal, int32_t tiles_per_bit, int32_t flags, int64_t* plan_out);
+
 #ifdef __cplusplus
 }
 #endif
