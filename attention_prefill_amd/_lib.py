@@ -62,6 +62,10 @@ def load():
         lib.attn_fwd_unfused_stream.restype = _I
         lib.attn_debug_plan.argtypes = [_I] * 9 + [ctypes.POINTER(ctypes.c_int64)]
         lib.attn_debug_plan.restype = _I
+        lib.attn_debug_route_trace.argtypes = fwd_args + [_I, _P, ctypes.c_int64, _P]
+        lib.attn_debug_route_trace.restype = _I
+        lib.attn_debug_check_cu_seqlens.argtypes = [_P, _I, _I]
+        lib.attn_debug_check_cu_seqlens.restype = _I
         _lib = lib
     return _lib
 
@@ -130,6 +134,31 @@ def _shapes(q, k, cu_seqlens):
     return B, qsl, ksl, d, n_qh, n_kvh
 
 
+def route_words_per_row(ksl, tiles_per_bit):
+    """uint32 words per bitmask row: ceil(ceil(ceil(ksl / 64) / tiles_per_bit) / 32)."""
+    n_g = -(-(-(-ksl // 64)) // tiles_per_bit)
+    return -(-n_g // 32)
+
+
+def _check_route_size(route_bitmask, qsl, ksl, tiles_per_bit, cu_seqlens):
+    """The words the kernel reads (include/attn.h): ceil(qsl/64) rows dense;
+    packed, one row per 64-row query tile of each sequence, at least
+    ceil(T/64) rows (the exact count, from the lengths, under
+    ATTN_DEBUG_VALIDATE=1, which reads cu_seqlens back from the device)."""
+    if route_bitmask is None:
+        return
+    if int(tiles_per_bit) < 1:
+        return      # the library reports ATTN_ERR_ARG
+    wpr = route_words_per_row(ksl, int(tiles_per_bit))
+    rows = -(-qsl // 64)
+    if cu_seqlens is not None and os.environ.get("ATTN_DEBUG_VALIDATE") == "1":
+        cu = cu_seqlens.cpu().tolist()
+        rows = sum(-(-(b - a) // 64) for a, b in zip(cu[:-1], cu[1:]) if b > a)
+    if route_bitmask.numel() < rows * wpr:
+        raise ValueError("route_bitmask holds %d words; the kernel reads %d (%d rows of %d words)"
+                         % (route_bitmask.numel(), rows * wpr, rows, wpr))
+
+
 def _out_route(q, out, route_bitmask):
     import torch
     if route_bitmask is not None:
@@ -165,6 +194,7 @@ def attn_fwd(q, k, v, out=None, *, scale=None, causal=False, cu_seqlens=None,
         raise ValueError("k and v must have the same shape")
     B, qsl, ksl, d, n_qh, n_kvh = _shapes(q, k, cu_seqlens)
     out = _out_route(q, out, route_bitmask)
+    _check_route_size(route_bitmask, qsl, ksl, tiles_per_bit, cu_seqlens)
     if scale is None:
         scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     if lowp == "int8":
@@ -206,6 +236,39 @@ def attn_debug_route_dump(route_bitmask, qsl, ksl, causal, tiles_per_bit, device
     return out
 
 
+def attn_debug_route_trace(q, k, v, route_bitmask, *, scale=None, causal=False, cu_seqlens=None,
+                           tiles_per_bit=4, lowp="int8", stream=None):
+    """(out, trace): a routed forward call that also records the tiles its
+    workgroups visit.  trace is int64 [rows, ceil(ksl/64)] (rows = bitmask
+    rows, packed: the bound ceil(T/64) + B): per tile, the number of FP16
+    visits plus 0x10000 times the number of low-precision visits."""
+    import torch
+    _need(q, "q", torch.float16)
+    _need(k, "k", torch.float16)
+    _need(v, "v", torch.float16)
+    B, qsl, ksl, d, n_qh, n_kvh = _shapes(q, k, cu_seqlens)
+    out = _out_route(q, None, route_bitmask)
+    _check_route_size(route_bitmask, qsl, ksl, tiles_per_bit, cu_seqlens)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    n_kt = -(-ksl // 64)
+    rows = -(-qsl // 64) + (B if cu_seqlens is not None else 0)
+    trace = torch.empty((rows, n_kt), dtype=torch.int32, device=q.device)
+    _check(load().attn_debug_route_trace(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, qsl, ksl, d, n_qh, n_kvh,
+                                         float(scale), int(bool(causal)), _ptr(cu_seqlens), _ptr(route_bitmask),
+                                         int(tiles_per_bit), LOWP[lowp], _ptr(trace), trace.numel(),
+                                         _stream(stream)))
+    return out, trace.to(torch.int64) & 0xffffffff
+
+
+def attn_debug_check_cu_seqlens(cu_seqlens, T):
+    """The ATTN_DEBUG_VALIDATE rule on a host int32 array (numpy); raises
+    AttnError when it fails.  No device needed."""
+    import numpy as np
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    _check(load().attn_debug_check_cu_seqlens(cu.ctypes.data_as(ctypes.c_void_p), int(cu.size - 1), int(T)))
+
+
 def attn_fwd_kv8_stream(q, k8, k_scale, v8, v_scale, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal,
                         cu_seqlens=None, route_bitmask=None, tiles_per_bit=4, stream=None):
     """Direct mirror of the C entry point (sizes passed explicitly)."""
@@ -233,6 +296,7 @@ def attn_fwd_kv8(q, k8, k_scale, v8, v_scale, out=None, *, scale=None, causal=Fa
         raise ValueError("k8/v8 must share a shape and k_scale/v_scale must be its leading dims")
     B, qsl, ksl, d, n_qh, n_kvh = _shapes(q, k8, cu_seqlens)
     out = _out_route(q, out, route_bitmask)
+    _check_route_size(route_bitmask, qsl, ksl, tiles_per_bit, cu_seqlens)
     if scale is None:
         scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
     attn_fwd_kv8_stream(q, k8, k_scale, v8, v_scale, out, B, qsl, ksl, d, n_qh, n_kvh, scale, causal,

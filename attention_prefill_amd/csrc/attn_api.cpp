@@ -9,7 +9,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <cstdlib>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "attn_internal.h"
 
@@ -83,30 +86,98 @@ attn_status validate(const attn::Problem& p) {
     return ATTN_OK;
 }
 
-// Scratch comes from the device's default stream-ordered pool.  Its release
-// threshold is raised once per device so that freed blocks stay cached for
-// the next call instead of going back to the system at every synchronise.
-void keep_pool_cached() {
-    static bool done[64] = {false};
+bool env_on(const char* name) {
+    const char* v = getenv(name);
+    return v && v[0] == '1' && v[1] == 0;
+}
+
+// Scratch comes from a stream-ordered memory pool that the library creates
+// for each device on first use and owns (the device's default pool and its
+// settings are left alone).  Its release threshold is the maximum, so freed
+// blocks stay cached in the pool for the next call instead of going back to
+// the system at every synchronise.
+attn_status scratch_pool(hipMemPool_t* out) {
+    static std::mutex mu;
+    static std::vector<hipMemPool_t> pools;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || done[dev]) return;
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)pools.size() <= dev) pools.resize(dev + 1, nullptr);
+    if (!pools[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        e = hipMemPoolCreate(&pool, &props);
+        if (e != hipSuccess) return hip_fail(e, "hipMemPoolCreate of the scratch pool");
         uint64_t keep = UINT64_MAX;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) {
+            (void)hipMemPoolDestroy(pool);
+            return hip_fail(e, "hipMemPoolSetAttribute of the scratch pool");
+        }
+        pools[dev] = pool;
     }
-    done[dev] = true;
+    *out = pools[dev];
+    return ATTN_OK;
+}
+
+attn_status scratch_alloc(void** ptr, size_t bytes, hipStream_t st) {
+    hipMemPool_t pool = nullptr;
+    attn_status ps = scratch_pool(&pool);
+    if (ps != ATTN_OK) return ps;
+    hipError_t e = hipMallocFromPoolAsync(ptr, bytes, pool, st);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocFromPoolAsync of scratch");
+    return ATTN_OK;
+}
+
+// The cu_seqlens rule of include/attn.h on a host copy: [0] = 0,
+// non-decreasing, [B] = T.
+attn_status check_cu_seqlens(const int32_t* cu, int B, int T) {
+    if (cu[0] != 0) return fail(ATTN_ERR_ARG, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+    for (int i = 0; i < B; ++i)
+        if (cu[i + 1] < cu[i])
+            return fail(ATTN_ERR_ARG, "cu_seqlens must be non-decreasing (cu_seqlens[%d] = %d > cu_seqlens[%d] = %d)",
+                        i, cu[i], i + 1, cu[i + 1]);
+    if (cu[B] != T) return fail(ATTN_ERR_ARG, "cu_seqlens[%d] must equal the total tokens %d (got %d)", B, T, cu[B]);
+    return ATTN_OK;
+}
+
+// Debug switches (environment, read at every call):
+//   ATTN_DEBUG_VALIDATE=1  copy cu_seqlens to the host (synchronising the
+//                          stream) and check its contents before launching;
+//   ATTN_DEBUG_SYNC=1      synchronise the stream after the launch and report
+//                          a failed kernel as ATTN_ERR_HIP from this call.
+attn_status debug_validate(const attn::Problem& p, hipStream_t st) {
+    if (!p.cu_seqlens || !env_on("ATTN_DEBUG_VALIDATE")) return ATTN_OK;
+    std::vector<int32_t> host((size_t)p.B + 1);
+    hipError_t e = hipMemcpyAsync(host.data(), p.cu_seqlens, host.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "ATTN_DEBUG_VALIDATE: reading cu_seqlens");
+    return check_cu_seqlens(host.data(), p.B, p.qsl);
+}
+
+attn_status debug_sync(hipStream_t st, const char* what) {
+    if (!env_on("ATTN_DEBUG_SYNC")) return ATTN_OK;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, what);
+    return ATTN_OK;
 }
 
 attn_status run_forward(const attn::Problem& p, hipStream_t st) {
     attn_status vs = validate(p);
     if (vs != ATTN_OK) return vs;
+    vs = debug_validate(p, st);
+    if (vs != ATTN_OK) return vs;
     void* scratch = nullptr;
     const size_t sbytes = attn::forward_scratch_bytes(p);
     if (sbytes) {
-        keep_pool_cached();
-        hipError_t e = hipMallocAsync(&scratch, sbytes, st);
-        if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of forward scratch");
+        vs = scratch_alloc(&scratch, sbytes, st);
+        if (vs != ATTN_OK) return vs;
     }
     hipError_t e = attn::launch_forward(p, scratch, st);
     if (scratch) {
@@ -114,6 +185,8 @@ attn_status run_forward(const attn::Problem& p, hipStream_t st) {
         if (e == hipSuccess) e = e2;
     }
     if (e != hipSuccess) return hip_fail(e, "attention forward launch");
+    vs = debug_sync(st, "attention forward (ATTN_DEBUG_SYNC)");
+    if (vs != ATTN_OK) return vs;
     g_last_error.clear();
     return ATTN_OK;
 }
@@ -127,14 +200,15 @@ attn_status run_unfused(const attn::Problem& p, hipStream_t st) {
     if ((double)p.B * p.n_qh * p.qsl * p.ksl * 6.0 > 64.0e9)
         return fail(ATTN_ERR_SHAPE, "unfused scores need %.1f GB of scratch (limit 64 GB)",
                     (double)p.B * p.n_qh * p.qsl * p.ksl * 6.0 / 1e9);
-    keep_pool_cached();
     void* scratch = nullptr;
-    hipError_t e = hipMallocAsync(&scratch, bytes, st);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync of unfused scratch");
-    e = attn::launch_unfused(p, scratch, st);
+    vs = scratch_alloc(&scratch, bytes, st);
+    if (vs != ATTN_OK) return vs;
+    hipError_t e = attn::launch_unfused(p, scratch, st);
     hipError_t e2 = hipFreeAsync(scratch, st);
     if (e == hipSuccess) e = e2;
     if (e != hipSuccess) return hip_fail(e, "unfused attention");
+    vs = debug_sync(st, "unfused attention (ATTN_DEBUG_SYNC)");
+    if (vs != ATTN_OK) return vs;
     g_last_error.clear();
     return ATTN_OK;
 }
@@ -253,6 +327,38 @@ attn_status attn_debug_plan(int32_t B, int32_t qsl, int32_t ksl, int32_t hdim, i
     for (int i = 0; i < 10; ++i) plan_out[i] = out[i];
     g_last_error.clear();
     return ATTN_OK;
+}
+
+attn_status attn_debug_route_trace(const void* q, const void* k, const void* v, void* out, int32_t B,
+                                   int32_t qsl, int32_t ksl, int32_t hdim, int32_t n_qh, int32_t n_kvh,
+                                   float scale, int32_t causal, const int32_t* cu_seqlens,
+                                   const uint32_t* route_bitmask, int32_t tiles_per_bit, int32_t lowp_format,
+                                   uint32_t* trace_out, int64_t trace_words, void* hip_stream) {
+    if (!route_bitmask) return fail(ATTN_ERR_NULL, "the route trace needs a routing bitmask");
+    if (!trace_out) return fail(ATTN_ERR_NULL, "trace_out must be a non-null device pointer");
+    if (!aligned4(trace_out)) return fail(ATTN_ERR_ARG, "trace_out must be 4-byte aligned");
+    attn::Problem p{q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal != 0,
+                    cu_seqlens, route_bitmask, tiles_per_bit};
+    p.lowp = lowp_format;
+    attn_status vs = validate(p);
+    if (vs != ATTN_OK) return vs;
+    const long long n_kt = (ksl + 63) / 64;
+    const long long rows = cu_seqlens ? (qsl + 63) / 64 + B : (qsl + 63) / 64;
+    if (trace_words < rows * n_kt)
+        return fail(ATTN_ERR_SHAPE, "trace_out needs %lld words (got %lld)", rows * n_kt, (long long)trace_words);
+    hipStream_t st = (hipStream_t)hip_stream;
+    hipError_t e = hipMemsetAsync(trace_out, 0, (size_t)trace_words * sizeof(uint32_t), st);
+    if (e != hipSuccess) return hip_fail(e, "clearing trace_out");
+    p.trace = trace_out;
+    return run_forward(p, st);
+}
+
+attn_status attn_debug_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t B, int32_t T) {
+    if (!cu_seqlens_host) return fail(ATTN_ERR_NULL, "cu_seqlens_host is null");
+    if (B <= 0) return fail(ATTN_ERR_SHAPE, "B must be positive (got %d)", B);
+    attn_status vs = check_cu_seqlens(cu_seqlens_host, B, T);
+    if (vs == ATTN_OK) g_last_error.clear();
+    return vs;
 }
 
 attn_status attn_debug_route_dump(const uint32_t* route_bitmask, int32_t qsl, int32_t ksl,

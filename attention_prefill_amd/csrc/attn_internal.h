@@ -26,6 +26,10 @@ struct Problem {
     const float* v_scale = nullptr;
     // what a set routing bit selects: 0 INT8, 1 FP8 e4m3 (rowwise scales)
     int lowp = 0;
+    // test hook (routed calls): device uint32 [bitmask rows, ceil(ksl / 64)],
+    // zeroed by the caller; every workgroup adds 1 (FP16) or 0x10000 (low
+    // precision) at each key tile it visits
+    uint32_t* trace = nullptr;
 };
 
 // Device scratch a forward call needs (bytes): quantised K rows for routed

@@ -83,6 +83,18 @@ constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23
 // index stride): reads beyond num_records return zero.
 constexpr int BUF_DWORD3 = 0x00020000;
 
+// The buffer resource of tile kt of a slab of `bytes` bytes cut into tiles
+// of `tile` bytes: based at the tile's first byte and holding only the bytes
+// left in the slab (none for a tile past its end).  Tile loads keep their
+// per-lane offset in the VGPR offset and pass no scalar offset, so the
+// descriptor's range check covers every byte they read: reads past the end
+// of the slab return zero and never touch the memory that follows it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes, int tile, int kt) {
+    const int o = __builtin_amdgcn_readfirstlane(kt * tile);
+    const int n = bytes > o ? bytes - o : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + o), (short)0, n, BUF_DWORD3);
+}
+
 // ---------------------------------------------------------------------------
 // INT8 quantisation rule shared by the K pass, the query prologue and the
 // test hook.
@@ -210,12 +222,41 @@ __device__ __forceinline__ u32x2 widen_i8x4(unsigned w) {
 }
 
 // ---------------------------------------------------------------------------
-// Routing decode: bit of group kt / tiles_per_bit in the row of query tile qt.
+// Routing decode.  One bitmask row belongs to one 64-row query tile; bit g of
+// the row (word g / 32, bit g % 32, least significant first) routes the group
+// of key tiles [g * tiles_per_bit, (g + 1) * tiles_per_bit): 1 = the
+// low-precision score path, 0 = FP16.  The cursor walks a key-tile range
+// [t, end) of one route: next(t, c) is the first tile >= t whose group's bit
+// is c, or end.  It scans the cached word with a count of trailing zeros
+// (of ~word for route 0) and reads a new word every 32 groups; a start
+// inside a group or a word is allowed.  Every value is uniform over the
+// wavefront.  The forward kernel's routed passes and the route-dump test
+// hook both walk their tiles with this cursor.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool route_bit(const uint32_t* row, int kt, int tiles_per_bit) {
-    int gi = kt / tiles_per_bit;
-    return (row[gi >> 5] >> (gi & 31)) & 1u;
-}
+struct RouteCursor {
+    const uint32_t* row;
+    int tpb;      // key tiles per bit
+    int end;      // one past the last tile of the range
+    int wi;       // index of the cached word, -1 for none
+    uint32_t w;   // the cached word
+
+    __device__ __forceinline__ RouteCursor(const uint32_t* r, int tiles_per_bit, int e)
+        : row(r), tpb(tiles_per_bit), end(e), wi(-1), w(0) {}
+
+    __device__ __forceinline__ int next(int t, bool c) {
+        while (t < end) {
+            const int gi = __builtin_amdgcn_readfirstlane(t / tpb);
+            if ((gi >> 5) != wi) {
+                wi = gi >> 5;
+                w = __builtin_amdgcn_readfirstlane(row[wi]);
+            }
+            const uint32_t wv = (c ? w : ~w) >> (gi & 31);
+            if (wv) return min(end, max(t, (gi + (int)__builtin_ctz(wv)) * tpb));
+            t = (wi + 1) * 32 * tpb;
+        }
+        return end;
+    }
+};
 
 // ---------------------------------------------------------------------------
 // LDS layout of one stage: the K tile (fp16 [key][d], or INT8 codes
@@ -269,6 +310,9 @@ struct FwdArgs {
     float* part_o;          // split partials: [ksplit, rows, HD] O / l (fp32)
     float* part_l;          // and [ksplit, rows] log2 of the softmax denominator, base-2 units
     long long part_rows;    // output rows (B * n_qh * qsl, or n_qh * T)
+    uint32_t* trace;        // test hook (routed calls), or null: visit counts per
+                            // (bitmask row, key tile), +1 FP16, +0x10000 low precision
+    int trace_nkt;          // key tiles per trace row
 };
 
 // Running max starts finite so that no exp2 argument is ever (-inf) - (-inf).
@@ -395,27 +439,23 @@ void attn_fwd_kernel(FwdArgs a) {
 
     i32x4 q8[ROUTED ? HD / 32 : 1];     // INT8 query codes (routed), set after the prologue wait
     float sq_mul = 1.0f;
+    // INT8 value cache: the value scales enter P relative to a power of two
+    // (vfac = 2^-e, with 2^e near the largest scale of the workgroup's key
+    // range), which the epilogue multiplies back (vfac_inv, exact)
+    float vfac = 1.0f, vfac_inv = 1.0f;
 
     // ---- tile loader ------------------------------------------------------------
     // K: 16-byte chunks of rows.  V: per thread a block of 4 keys x 8 d, read as
     // four 16-byte row pieces and written transposed as eight 8-byte pieces.
-    // Loads go through buffer descriptors covering exactly this sequence's
-    // rows: reads past the last key return zeros (those keys are masked to
-    // -inf, so P is exactly 0 there), the per-lane offsets are loop
-    // invariant and the tile advance is a scalar offset, so nothing in the
-    // loop waits on the loads of the next tile before its LDS store.
+    // Loads go through buffer resources covering one tile and the rest of this
+    // sequence's rows (tile_rsrc): reads past the last key return zeros
+    // (those keys are masked to -inf, so P is exactly 0 there), and the
+    // per-lane offsets are loop invariant, so nothing in the loop waits on
+    // the loads of the next tile before its LDS store.
     const int slab = Lk * HD * 2;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, slab, BUF_DWORD3);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, slab, BUF_DWORD3);
-    __amdgpu_buffer_rsrc_t k8rs = krs, skrs = krs, v8rs = krs, svrs = krs;
-    if constexpr (ROUTED || KV8) {
-        k8rs = __builtin_amdgcn_make_buffer_rsrc((void*)k8b, (short)0, Lk * HD, BUF_DWORD3);
-        skrs = __builtin_amdgcn_make_buffer_rsrc((void*)skb, (short)0, Lk * 4, BUF_DWORD3);
-    }
-    if constexpr (KV8) {
-        v8rs = __builtin_amdgcn_make_buffer_rsrc((void*)v8b, (short)0, Lk * HD, BUF_DWORD3);
-        svrs = __builtin_amdgcn_make_buffer_rsrc((void*)svb, (short)0, Lk * 4, BUF_DWORD3);
-    }
+    constexpr int TB16 = BN * HD * 2;     // bytes of an fp16 K or V tile
+    constexpr int TB8 = BN * HD;          // bytes of an INT8 K or V tile
+    constexpr int TBS = BN * 4;           // bytes of a tile's per-key scales
     // Staging registers of one tile between its global loads and its LDS
     // store.  With PF = 2 two sets alternate, so the loads of tile t+2 are
     // issued while tile t is computed and have two tiles' time to land.
@@ -443,17 +483,17 @@ void attn_fwd_kernel(FwdArgs a) {
     // wait-count analysis sees one straight path.
     static_assert(PF == 1 || ((BN / 4) * (HD / 8) == NT / 2 && BN * HD / 8 == 4 * (NT / 2)),
                   "balanced loader shape");
-    const __amdgpu_buffer_rsrc_t rs2 = v_half ? vrs : krs;
+    const _Float16* base2 = v_half ? vb : kb;
     int voff2[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         voff2[i] = v_half ? ((4 * (th % (BN / 4)) + i) * HD + 8 * (th / (BN / 4))) * 2
                           : (th + i * (NT / 2)) * 16;
     auto gload2 = [&](Staging2& sg, int kt) __attribute__((always_inline)) {
-        const int soff = kt * BN * HD * 2;
+        const __amdgpu_buffer_rsrc_t rs2 = tile_rsrc(base2, slab, TB16, kt);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            sg.r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs2, voff2[i], soff, 0));
+            sg.r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs2, voff2[i], 0, 0));
     };
     auto lstore2 = [&](const Staging2& sg, int stage) __attribute__((always_inline)) {
         char* kbuf = smem + (stage * KS + kgp) * L::STAGE;
@@ -485,26 +525,28 @@ void attn_fwd_kernel(FwdArgs a) {
         u32x4(&vreg)[VB][4] = sg.vreg;
         u32x4& skreg = sg.skreg;
         if (KV8 || (ROUTED && i8)) {
-            const int soff = kt * BN * HD;
+            const __amdgpu_buffer_rsrc_t k8rs = tile_rsrc(k8b, Lk * HD, TB8, kt);
 #pragma unroll
             for (int n = 0; n < K8CH; ++n) {
                 const int c = tid + n * NT;     // row c / (HD/16), 16-byte column c % (HD/16)
                 if (K8TOT % NT == 0 || c < K8TOT)
-                    kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k8rs, c * 16, soff, 0));
+                    kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k8rs, c * 16, 0, 0));
             }
-            if (tid < BN / 4)
-                skreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(skrs, tid * 16, kt * BN * 4, 0));
+            if (tid < BN / 4) {
+                const __amdgpu_buffer_rsrc_t skrs = tile_rsrc(skb, Lk * 4, TBS, kt);
+                skreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(skrs, tid * 16, 0, 0));
+            }
         } else {
-            const int soff = kt * BN * HD * 2;
+            const __amdgpu_buffer_rsrc_t krs = tile_rsrc(kb, slab, TB16, kt);
 #pragma unroll
             for (int n = 0; n < KCH; ++n) {
                 const int c = tid + n * NT;     // row c / (HD/8), 16-byte column c % (HD/8)
                 if (KTOT % NT == 0 || c < KTOT)
-                    kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, c * 16, soff, 0));
+                    kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, c * 16, 0, 0));
             }
         }
         if constexpr (KV8) {
-            const int soff = kt * BN * HD;
+            const __amdgpu_buffer_rsrc_t v8rs = tile_rsrc(v8b, Lk * HD, TB8, kt);
 #pragma unroll
             for (int n = 0; n < VB; ++n) {
                 const int bi = tid + n * NT;
@@ -514,14 +556,16 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         sg.v8reg[n][i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                            v8rs, (4 * kg + i) * HD + 8 * dc, soff, 0));
+                            v8rs, (4 * kg + i) * HD + 8 * dc, 0, 0));
                 }
             }
-            if (tid >= BN / 4 && tid < BN / 2)
+            if (tid >= BN / 4 && tid < BN / 2) {
+                const __amdgpu_buffer_rsrc_t svrs = tile_rsrc(svb, Lk * 4, TBS, kt);
                 sg.svreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    svrs, (tid - BN / 4) * 16, kt * BN * 4, 0));
+                    svrs, (tid - BN / 4) * 16, 0, 0));
+            }
         } else {
-            const int soff = kt * BN * HD * 2;
+            const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vb, slab, TB16, kt);
 #pragma unroll
             for (int n = 0; n < VB; ++n) {
                 const int bi = tid + n * NT;
@@ -531,7 +575,7 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         vreg[n][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                            vrs, ((4 * kg + i) * HD + 8 * dc) * 2, soff, 0));
+                            vrs, ((4 * kg + i) * HD + 8 * dc) * 2, 0, 0));
                 }
             }
         }
@@ -611,7 +655,7 @@ void attn_fwd_kernel(FwdArgs a) {
             }
         }
         if (KV8 && tid >= BN / 4 && tid < BN / 2)
-            *(f32x4*)(scl + BN + 4 * (tid - BN / 4)) = __builtin_bit_cast(f32x4, sg.svreg);
+            *(f32x4*)(scl + BN + 4 * (tid - BN / 4)) = __builtin_bit_cast(f32x4, sg.svreg) * vfac;
     };
 
     // ---- state --------------------------------------------------------------------
@@ -823,6 +867,33 @@ void attn_fwd_kernel(FwdArgs a) {
     auto has = [&](int it) __attribute__((always_inline)) { return it < n_it && kt_first + KS * it < kt1; };
 
     const int kt_end = min(w_nkt, kt1);
+
+    if constexpr (KV8) {
+        // The value-cache scales multiply P before its fp16 rounding.  P
+        // reaches 2^TAU between rescales, so the scales are first brought to
+        // [1, 2) at their largest by an exact power of two: p * s_v * vfac
+        // stays below 2^(TAU+1) (no overflow for any scale), and keys whose
+        // scale is near the largest keep full fp16 precision whatever the
+        // value magnitude (no subnormal P for small values).
+        float mx = 0.0f;
+        const int j1 = min(kt1 * BN, Lk);
+        for (int j = kt0 * BN + (int)threadIdx.x; j < j1; j += NW * KS * 64) mx = fmaxf(mx, fabsf(svb[j]));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        float* red = (float*)smem;
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+        __syncthreads();
+        mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NW * KS; ++i) mx = fmaxf(mx, red[i]);
+        __syncthreads();
+        const int e = (int)((u_from_f(mx) >> 23) & 0xffu);    // biased exponent
+        if (e != 0 && e != 255) {
+            const int sh = max(-126, min(126, 127 - e));       // mx * 2^sh in [1, 2)
+            vfac = f_from_u((unsigned)(127 + sh) << 23);
+            vfac_inv = f_from_u((unsigned)(127 - sh) << 23);
+        }
+    }
     auto query_prologue = [&]() __attribute__((always_inline)) {
         if (a.neg) {
 #pragma unroll
@@ -836,23 +907,11 @@ void attn_fwd_kernel(FwdArgs a) {
         // state does not depend on the order of the tiles).  The bitmask word
         // in use is cached; a new word is read every 32 groups.
         static_assert(KS == 1 && PF == 1 && BN == TK, "routed calls: one key group of 64-key tiles");
-        const int tpb = a.tiles_per_bit;
-        int wi_c = -1;
-        uint32_t w_c = 0;
+        RouteCursor cur(rrow, a.tiles_per_bit, kt1);
         // first tile >= t of this workgroup's range whose route is c, else kt1
-        auto next_of = [&](int t, bool c) __attribute__((always_inline)) {
-            while (t < kt1) {
-                const int gi = __builtin_amdgcn_readfirstlane(t / tpb);
-                if ((gi >> 5) != wi_c) {
-                    wi_c = gi >> 5;
-                    w_c = __builtin_amdgcn_readfirstlane(rrow[wi_c]);
-                }
-                const uint32_t wv = (c ? w_c : ~w_c) >> (gi & 31);
-                if (wv) return min(kt1, max(t, (gi + (int)__builtin_ctz(wv)) * tpb));
-                t = (wi_c + 1) * 32 * tpb;
-            }
-            return kt1;
-        };
+        auto next_of = [&](int t, bool c) __attribute__((always_inline)) { return cur.next(t, c); };
+        // test hook: count every tile the workgroup visits, by route
+        uint32_t* const trace = a.trace ? a.trace + (size_t)(rrow0 + m0 / TQ) * a.trace_nkt : nullptr;
         int st = 0;
         // tiles [kt, kt1) of route C: the first (kt) already in LDS stage st
         // and, with four stages, the second in stage st+1; with four stages
@@ -866,6 +925,7 @@ void attn_fwd_kernel(FwdArgs a) {
             int si = 0;
             auto step = [&](auto mask_tag) __attribute__((always_inline)) {
                 constexpr bool MASK = decltype(mask_tag)::value;
+                if (trace && tid == 0) atomicAdd(trace + kt, C ? 0x10000u : 1u);
                 if constexpr (NST == 4) {
                     if (kn2 < kt1) gload(set0, kn2, C);
                     if (MASK ? kt < kt_end : wave_active) tile(mask_tag, st, kt, C);
@@ -1046,7 +1106,7 @@ void attn_fwd_kernel(FwdArgs a) {
             // keys of this split: O / l and m + log2(l); a split with no visible key
             // for the row contributes nothing (-inf)
             const bool any = l_tot > 0.0f;
-            const float inv_l = any ? 1.0f / l_tot : 0.0f;
+            const float inv_l = any ? vfac_inv / l_tot : 0.0f;
             const size_t prow = (size_t)split * a.part_rows + qrow0 + qi;
             float* po = a.part_o + prow * HD + 4 * g;
 #pragma unroll
@@ -1063,7 +1123,7 @@ void attn_fwd_kernel(FwdArgs a) {
         return;
     }
     if (wave_active && qi < Lq) {
-        const float inv_l = 1.0f / l_tot;
+        const float inv_l = vfac_inv / l_tot;
         _Float16* op = ob + (size_t)qi * HD + 4 * g;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -1181,19 +1241,27 @@ __global__ __launch_bounds__(64) void quantize_qrows_kernel(const _Float16* __re
     }
 }
 
-// Test hook: the route each (query tile, key tile) takes in the forward kernel.
-__global__ void route_dump_kernel(const uint32_t* route, int qsl, int ksl, int causal,
-                                  int tiles_per_bit, int wpr, uint8_t* out) {
+// Test hook: the route each (query tile, key tile) takes, walked with the
+// forward kernel's cursor and legality rule.  One wavefront per query tile
+// (every lane walks the same, uniform, cursor; lane 0 writes): the tiles of
+// the causally visible range [0, n_vis) take route 0 or 1, the rest 2.
+__global__ __launch_bounds__(64) void route_dump_kernel(const uint32_t* route, int qsl, int ksl, int causal,
+                                                        int tiles_per_bit, int wpr, uint8_t* out) {
     const int n_kt = (ksl + TK - 1) / TK;
-    const int n_qt = (qsl + TQ - 1) / TQ;
-    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long long)n_qt * n_kt) return;
-    const int qt = (int)(idx / n_kt), kt = (int)(idx % n_kt);
+    const int qt = blockIdx.x;
     const int last_row = min(qt * TQ + TQ, qsl) - 1;
-    const bool visited = !causal || kt * TK <= last_row + (ksl - qsl);
-    uint8_t r = 2;
-    if (visited) r = (route != nullptr && route_bit(route + (size_t)qt * wpr, kt, tiles_per_bit)) ? 1 : 0;
-    out[idx] = r;
+    const int n_vis = causal ? min(n_kt, (last_row + (ksl - qsl)) / TK + 1) : n_kt;
+    uint8_t* o = out + (size_t)qt * n_kt;
+    for (int kt = threadIdx.x; kt < n_kt; kt += 64) o[kt] = 2;
+    __syncthreads();
+    if (route == nullptr) {
+        for (int kt = threadIdx.x; kt < n_vis; kt += 64) o[kt] = 0;
+        return;
+    }
+    RouteCursor cur(route + (size_t)qt * wpr, tiles_per_bit, n_vis);
+    for (int c = 0; c < 2; ++c)
+        for (int kt = cur.next(0, c != 0); kt < n_vis; kt = cur.next(kt + 1, c != 0))
+            if (threadIdx.x == 0) o[kt] = (uint8_t)c;
 }
 
 template <typename K>
@@ -1290,9 +1358,8 @@ hipError_t launch_route_dump(const uint32_t* route, int qsl, int ksl, bool causa
     const int n_qt = (qsl + TQ - 1) / TQ;
     const int n_g = (n_kt + tiles_per_bit - 1) / tiles_per_bit;
     const int wpr = (n_g + 31) / 32;
-    const long long n = (long long)n_qt * n_kt;
-    const int grid = (int)((n + 255) / 256);
-    hipLaunchKernelGGL(route_dump_kernel, dim3(grid), dim3(256), 0, st, route, qsl, ksl,
+    (void)n_kt;
+    hipLaunchKernelGGL(route_dump_kernel, dim3(n_qt), dim3(64), 0, st, route, qsl, ksl,
                        causal ? 1 : 0, tiles_per_bit, wpr, out);
     return hipGetLastError();
 }
@@ -1479,6 +1546,8 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
     a.part_rows = pl.out_rows;
     a.part_o = pl.ksplit > 1 ? (float*)((char*)scratch + pl.po_off) : nullptr;
     a.part_l = pl.ksplit > 1 ? (float*)((char*)scratch + pl.pl_off) : nullptr;
+    a.trace = p.route ? p.trace : nullptr;
+    a.trace_nkt = (p.ksl + TK - 1) / TK;
     const bool varlen = p.cu_seqlens != nullptr;
     const bool routed = p.route != nullptr;
 

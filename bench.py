@@ -4,18 +4,24 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole forward path over the workload's batch of
-synthetic input (for the default workload: one non-causal and one causal
-call on the same Q/K/V).  Inputs are resident in HBM before the timed
-region starts.  The value is the throughput convention of the "Nax Refactor"
-timing tables (ml-explore/mlx pull request 3271): 4*B*n_qh*qsl*ksl*hdim FLOP
-per call, halved when causal, divided by wall time.  Before the W warmup
-steps, untimed steps run for about one second (--settle-ms), so that the GPU
-clock has left its idle level before anything is timed.
+synthetic input.  The default workload is the largest configuration: the
+TileMix-routed causal prefill of 16384 tokens (hdim 128, 32 query heads over
+8 kv heads, 4 key tiles per routing bit, bits drawn Bernoulli(0.5)), one
+forward call per step; its all-FP16 run (the same inputs and kernel with a
+zero bitmask) is timed in the same invocation and reported in the same line.
+Inputs are resident in HBM before the timed region starts.  The value is the
+throughput convention of the "Nax Refactor" timing tables (ml-explore/mlx
+pull request 3271): 4*B*n_qh*qsl*ksl*hdim FLOP per call, halved when causal,
+divided by wall time.  Before the W warmup steps, untimed steps run for about
+one second (--settle-ms), so that the GPU clock has left its idle level
+before anything is timed.
 
 Printed: one JSON line with the metric, a roofline record of the dominant
 kernel (its per-launch time measured with HIP events on its own stream, in a
 second pass over the same steps, since event records cost GPU time of their
-own) and the CPU oracle's throughput on a bounded sample of the same workload.
+own; routed kernels are priced against the fp16/INT8 mixed MFMA peak of
+their drawn bitmask) and the CPU oracle's throughput on a bounded sample of
+the same workload.
 """
 import argparse
 import hashlib
@@ -44,7 +50,9 @@ PAGE_ROWS = {  # (qsl, ksl, hdim, n_qh, n_kvh, causal) -> (t_fus for 64 calls, t
     (512, 4096, 128, 32, 8, 1): (0.168, 6.548),
 }
 
-# default workload: dense 1024 x 1024, hdim 64, 32 heads, non-causal + causal
+DEFAULT_WORKLOAD = "tilemix_16384_d128_causal"
+# named sets of calls per step: the 1024-token pair is the page's first
+# two "After" rows (one non-causal and one causal call on the same Q/K/V)
 BENCH_SETS = {
     "dense_1024_d64_pair": ["dense_1024_d64", "dense_1024_d64_causal"],
 }
@@ -63,12 +71,15 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=1000.0,
                     help="before the warmup steps, run untimed steps until this much wall time has "
                          "passed, so that the GPU clock has reached its sustained level (0: none)")
-    ap.add_argument("--workload", default="dense_1024_d64_pair", choices=sorted(BENCH_SETS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(BENCH_SETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the all-FP16 and dense runs of a routed workload (for profiler runs whose "
+                         "per-kernel averages must cover the drawn bitmask only)")
     ap.add_argument("--fp16-compare", action="store_true",
-                    help="routed workloads: also time the same inputs with an all-FP16 (zero) "
-                         "bitmask and with no bitmask; INT8-cache workloads: also time the "
-                         "fp16 K and V the cache was encoded from")
+                    help="INT8-cache workloads: also time the fp16 K and V the cache was encoded "
+                         "from (routed workloads always time their all-FP16 run and the dense "
+                         "kernel on the same inputs)")
     ap.add_argument("--unfused-compare", action="store_true",
                     help="dense fp16 workloads: also time the unfused baseline (score GEMM, masked "
                          "softmax, P.V GEMM) on the same inputs, the page's t_unfs / speed_up")
@@ -134,11 +145,32 @@ class Call:
         return go
 
 
+def host_cpu():
+    """(logical CPUs of the host, CPUs this process may run on, CPU model)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count() or 1
+    return os.cpu_count() or 1, allowed, model
+
+
 def cpu_baseline(calls, budget_s=12.0):
     """The oracle, untuned, on a bounded sample: whole query heads of each call
-    (full sequence length, the same inputs), as many as fit the time budget."""
+    (full sequence length, the same inputs), as many as fit the time budget.
+    Threads: every CPU this process may run on, or OMP_NUM_THREADS when the
+    host sets it (the GPU's share of a shared host)."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(16, os.cpu_count() or 1)
+    nproc, allowed, model = host_cpu()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or allowed
     flop = secs = 0.0
     samples = []
     for c in calls:
@@ -177,7 +209,31 @@ def cpu_baseline(calls, budget_s=12.0):
         secs += spent
         samples.append("%s: %d of %d query heads" % (w.name, heads, w.n_qh))
     return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "; ".join(samples) + ", full sequence length, same inputs; %.1f s" % secs}
+            "sample": "; ".join(samples) + ", full sequence length, same inputs; %.1f s" % secs,
+            "host_logical_cpus": nproc, "process_cpus": allowed, "cpu_model": model,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
+def int8_share(w, route):
+    """Share of the visited score (QK^T) pairs that a drawn bitmask sends to
+    the low-precision route: bits decoded LSB-first, each (query tile, key
+    tile) counted by its causally visible pairs."""
+    T = 64
+    n_kt = -(-w.ksl // T)
+    n_g = -(-n_kt // w.tiles_per_bit)
+    bits = np.unpackbits(np.ascontiguousarray(route, dtype=np.uint32).view(np.uint8).reshape(route.shape[0], -1),
+                         axis=1, bitorder="little")[:, :n_g].astype(bool)
+    off = w.ksl - w.qsl if w.causal else 0
+    low = tot = 0
+    for qt in range(-(-w.qsl // T)):
+        rows = np.arange(qt * T, min(qt * T + T, w.qsl))
+        lim = np.minimum(w.ksl, rows + off + 1) if w.causal else np.full(rows.size, w.ksl)
+        for kt in range(n_kt):
+            pairs = int(np.clip(lim - kt * T, 0, min(T, w.ksl - kt * T)).sum())
+            tot += pairs
+            if bits[qt, kt // w.tiles_per_bit]:
+                low += pairs
+    return low / tot if tot else 0.0
 
 
 def hbm_traffic(workload, dominant_name):
@@ -289,11 +345,24 @@ def main():
                                                    (" routed" + (" fp8" if dw.lowp == "fp8" else ""))
                                                    if dw.tiles_per_bit else "",
                                                    " kv8" if dw.kv8 else "")
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / FP16_PEAK_TFLOPS, 4),
+    # Peak: dense fp16 MFMA, or for a routed kernel the mixed peak of its
+    # drawn bitmask: with a share f of the score FLOP (half of all FLOP) on
+    # the INT8 / FP8 MFMA at twice the fp16 rate, the MFMA time floor is
+    # F / P16 * (1 - f / 4).
+    peak = FP16_PEAK_TFLOPS
+    share = None
+    if dc.route_host is not None:
+        share = int8_share(dw, dc.route_host)
+        peak = FP16_PEAK_TFLOPS / (1.0 - share / 4.0)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": hbm_traffic(args.workload, dom_name), "kernel": dom_name,
                 "flop_per_launch": dc.visited_flop, "avg_launch_ms": round(dom_ms, 5),
                 "ms_per_step_with_events": round((te1 - te0) / args.steps * 1e3, 5)}
+    if share is not None:
+        roofline.update({"peak_kind": "fp16/%s mixed MFMA for the drawn bitmask" % dw.lowp,
+                         "lowp_share_of_score_flop": round(share, 4), "peak_fp16": FP16_PEAK_TFLOPS,
+                         "frac_of_fp16_peak": round(achieved / FP16_PEAK_TFLOPS, 4)})
 
     # the page's figures for the same shapes, combined like the value
     page = []
@@ -302,6 +371,9 @@ def main():
         key = (w.qsl, w.ksl, w.hdim, w.n_qh, w.n_kvh, int(w.causal))
         if w.B == 1 and not w.varlen and not w.tiles_per_bit and not w.kv8 and key in PAGE_ROWS:
             page.append(PAGE_ROWS[key][0] / 64.0)
+    # vs_baseline: the page's own fused figure for exactly this workload (its
+    # hardware is not stated: context, not a same-machine speed-up); null for
+    # workloads the page does not time
     vs = None
     if len(page) == len(calls):
         vs = round(value / (metric_flop / sum(page) / 1e12), 3)
@@ -335,12 +407,15 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - ta) / args.steps
 
-    if args.fp16_compare and any(c.route is not None for c in calls):
+    if vs is not None:
+        rec["vs_baseline_note"] = "the page's fused time for these shapes; its hardware is not stated"
+    if any(c.route is not None for c in calls) and not args.no_compare:
         # the all-FP16 run of the same inputs: the same kernel with a zero
         # bitmask, and for context the dense kernel with no bitmask at all
         zero_step = time_route("zero")
         dense_step = time_route("none")
         rec["all_fp16_ms_per_step"] = round(zero_step * 1e3, 5)
+        rec["all_fp16_tflops"] = round(metric_flop / zero_step / 1e12, 3)
         rec["routed_speedup_vs_all_fp16"] = round(zero_step / sec_per_step, 4)
         rec["dense_no_bitmask_ms_per_step"] = round(dense_step * 1e3, 5)
         rec["routed_speedup_vs_dense"] = round(dense_step / sec_per_step, 4)

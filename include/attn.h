@@ -38,17 +38,29 @@
  *   the row of (s, qt) is qt + sum over s' < s of ceil(L_s'/64); wpr is
  *   computed with ksl = T, and bits of groups past the sequence's own key
  *   tiles are ignored.
+ *   Size: the bitmask must hold ceil(qsl / 64) * wpr words (dense), or
+ *   (sum over s of ceil(L_s / 64)) * wpr words (packed); the library cannot
+ *   see its length, and a shorter array is read past its end.
  * out is fully overwritten.  Nothing the caller passes is retained.
  *
  * Calls are asynchronous: they validate the arguments on the host, enqueue
  * work on the given stream and return.  Routed calls (quantised K rows) and
  * calls whose grid is split along the keys (fp32 partial results) use
- * stream-ordered device scratch from the device's default memory pool
- * (hipMallocAsync / hipFreeAsync on the same stream; the pool's release
- * threshold is raised once so blocks stay cached).  Errors are reported by
- * the return code; a
- * thread-local message is available from attn_last_error().  Argument
- * errors are detected before any device work is enqueued.
+ * stream-ordered device scratch (allocated and freed on the same stream) from
+ * a memory pool that the library creates per device on first use and keeps
+ * until the process ends; freed blocks stay cached in that pool for the next
+ * call.  The device's default pool is not touched.  Errors are reported by
+ * the return code; a thread-local message is available from
+ * attn_last_error().  Argument errors are detected before any device work is
+ * enqueued.
+ *
+ * The contents of cu_seqlens are the caller's responsibility: the kernels
+ * trust them.  Two environment switches help debugging (read at every call):
+ *   ATTN_DEBUG_VALIDATE=1  the forward entry points copy cu_seqlens to the
+ *     host (synchronising the stream) and return ATTN_ERR_ARG unless
+ *     cu_seqlens[0] = 0, it is non-decreasing and cu_seqlens[B] = T;
+ *   ATTN_DEBUG_SYNC=1  every entry point synchronises its stream after the
+ *     launch and returns ATTN_ERR_HIP if a kernel failed.
  */
 #ifndef ATTN_MI355X_H
 #define ATTN_MI355X_H
@@ -107,11 +119,14 @@ attn_status attn_fwd_stream(const void* q, const void* k, const void* v, void* o
  *   k8, v8: device int8 in the layout of k and v; 16-byte aligned.
  *   k_scale, v_scale: device fp32, one per K / V row ([B, n_kvh, ksl] dense,
  *   [n_kvh, T] packed); 4-byte aligned.
- * attn_quantize_rows builds such a cache from fp16 rows.  The value-cache
- * scale is folded into the fp16 probabilities that multiply the codes, so
- * p * v_scale must stay inside the fp16 range (v_scale = amax / 127 of a
- * row well inside it does).  Errors as attn_fwd (ATTN_ERR_NULL names the
- * cache pointers). */
+ * attn_quantize_rows builds such a cache from fp16 rows.  The value scales
+ * are applied to the fp16 probabilities that multiply the codes, after
+ * division by a power of two near the largest |v_scale| of the keys a
+ * workgroup visits (multiplied back, exactly, at the end), so any finite
+ * v_scale works without overflow, and the precision of p * v_scale in fp16
+ * depends only on the ratio of v_scale to that largest scale, not on the
+ * values' magnitude.  Errors as attn_fwd (ATTN_ERR_NULL names the cache
+ * pointers). */
 attn_status attn_fwd_kv8(const void* q, const int8_t* k8, const float* k_scale,
                          const int8_t* v8, const float* v_scale, void* out,
                          int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
@@ -185,14 +200,45 @@ attn_status attn_debug_quantize_rows(const void* x_f16, int32_t rows, int32_t hd
                                      int8_t* q8, float* scale_out, int32_t path,
                                      void* hip_stream);
 
-/* Test hook for the routing decode: writes, for every (query tile qt, key
- * tile kt) of a qsl x ksl problem, the route the attention kernel takes:
- * 0 = FP16, 1 = INT8, 2 = not visited (the causal mask leaves that tile
+/* Test hook for the routing decode (TileMix abstract: routing decisions
+ * packed into compact bitmasks): writes, for every (query tile qt, key tile
+ * kt) of a qsl x ksl problem, the route that the bitmask gives, decoded by
+ * the same device cursor the forward kernel's routed passes walk, over the
+ * same causally visible tile range: 0 = FP16, 1 = INT8 (or the
+ * low-precision route), 2 = not visited (the causal mask leaves that tile
  * empty for every row of qt).  route_out: device uint8 [ceil(qsl/64),
- * ceil(ksl/64)].  Asynchronous on hip_stream. */
+ * ceil(ksl/64)].  Asynchronous on hip_stream.  attn_debug_route_trace
+ * records what the forward kernel itself visits. */
 attn_status attn_debug_route_dump(const uint32_t* route_bitmask, int32_t qsl, int32_t ksl,
                                   int32_t causal, int32_t tiles_per_bit, uint8_t* route_out,
                                   void* hip_stream);
+
+/* Test hook: a routed forward call (the arguments and result of
+ * attn_fwd_lowp_stream; route_bitmask must be set) that also records the
+ * tiles its workgroups visit.  trace_out: device uint32 [rows, ceil(ksl/64)]
+ * with rows = ceil(qsl/64) (dense) or the packed bitmask's row count, row r
+ * holding the tiles of bitmask row r; trace_words is its length, which must
+ * be at least rows * ceil(ksl/64) (packed: (ceil(T/64) + B) * ceil(T/64)).
+ * The call clears it, then every workgroup adds 1 at each key tile it visits
+ * on the FP16 route and 0x10000 at each one it visits on the low-precision
+ * route, in the kernel's own routed loop.  A routed workgroup holds 32 or 64
+ * rows of one query tile (attn_debug_plan's rows per workgroup) for one
+ * workgroup column (batch element, kv head, query-head group), so a tile
+ * that every workgroup of its query tile visits reads n or n << 16, with n
+ * the number of such workgroups.  Asynchronous on hip_stream.  Not for
+ * production: the counts use device atomics. */
+attn_status attn_debug_route_trace(const void* q, const void* k, const void* v, void* out,
+                                   int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
+                                   int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                                   const int32_t* cu_seqlens, const uint32_t* route_bitmask,
+                                   int32_t tiles_per_bit, int32_t lowp_format,
+                                   uint32_t* trace_out, int64_t trace_words, void* hip_stream);
+
+/* Test hook for the cu_seqlens rule that ATTN_DEBUG_VALIDATE applies, on a
+ * HOST array of B + 1 entries: ATTN_OK if cu_seqlens_host[0] = 0, it is
+ * non-decreasing and cu_seqlens_host[B] = T, else ATTN_ERR_ARG with a message
+ * naming the entry.  No device access. */
+attn_status attn_debug_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t B, int32_t T);
 
 /* Test hook for the launch planner: the workgroup shape and grid that the
  * forward entry points would launch for these sizes.  Nothing is launched and

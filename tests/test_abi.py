@@ -27,7 +27,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for n in ["attn_fwd", "attn_fwd_stream", "attn_last_error", "attn_abi_version",
               "attn_debug_quantize_rows", "attn_debug_route_dump", "attn_fwd_kv8", "attn_fwd_kv8_stream",
-              "attn_quantize_rows", "attn_fwd_unfused_stream", "attn_fwd_lowp_stream"]:
+              "attn_quantize_rows", "attn_fwd_unfused_stream", "attn_fwd_lowp_stream", "attn_debug_plan",
+              "attn_debug_route_trace", "attn_debug_check_cu_seqlens"]:
         assert n in names
 
 
@@ -145,3 +146,60 @@ def test_product_path_never_imports_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_route_trace_hook_validates():
+    lib = A.load()
+    base = (FAKE, FAKE, FAKE, FAKE, 1, 128, 640, 64, 4, 2, 0.1, 0, None)
+    # no bitmask, no trace buffer, misaligned trace buffer, too few words
+    assert lib.attn_debug_route_trace(*base, None, 4, 0, FAKE, 40, None) == NULL
+    assert lib.attn_debug_route_trace(*base, FAKE, 4, 0, None, 40, None) == NULL
+    assert lib.attn_debug_route_trace(*base, FAKE, 4, 0, FAKE + 2, 40, None) == ARG
+    assert lib.attn_debug_route_trace(*base, FAKE, 4, 0, FAKE, 19, None) == SHAPE
+    assert "20 words" in A.attn_last_error()
+    # the forward rules still apply
+    assert lib.attn_debug_route_trace(*base, FAKE, 0, 0, FAKE, 40, None) == ARG
+    assert lib.attn_debug_route_trace(*base, FAKE, 4, 5, FAKE, 40, None) == ARG
+
+
+@pytest.mark.parametrize("cu,T,ok", [
+    ([0, 5, 5, 12], 12, True), ([0], 0, None), ([0, 0], 0, True), ([0, 64, 200], 200, True),
+    ([1, 5, 12], 12, False), ([0, 7, 5, 12], 12, False), ([0, 5, 11], 12, False), ([0, 5, 13], 12, False),
+    ([0, -1, 12], 12, False),
+])
+def test_cu_seqlens_rule_on_host_arrays(cu, T, ok):
+    """The rule ATTN_DEBUG_VALIDATE applies before a packed launch:
+    cu[0] = 0, non-decreasing, cu[B] = T (B = 0 is a shape error)."""
+    if ok is None:
+        with pytest.raises(A.AttnError) as e:
+            A.attn_debug_check_cu_seqlens(cu, T)
+        assert e.value.status == SHAPE
+        return
+    if ok:
+        A.attn_debug_check_cu_seqlens(cu, T)
+    else:
+        with pytest.raises(A.AttnError) as e:
+            A.attn_debug_check_cu_seqlens(cu, T)
+        assert e.value.status == ARG and "cu_seqlens" in str(e.value)
+
+
+def test_binding_checks_bitmask_length(orc):
+    """The binding rejects a bitmask shorter than the words the kernel reads
+    (ceil(qsl/64) rows of ceil(ceil(ceil(ksl/64)/tpb)/32) words); the row
+    width agrees with the oracle's bitmask layout."""
+    torch = pytest.importorskip("torch")
+    for ksl in (1, 64, 65, 2048, 2049, 8192, 8193, 16384, 70000):
+        for tpb in (1, 3, 4):
+            assert _lib.route_words_per_row(ksl, tpb) == orc.words_per_row(ksl, 64, tpb)
+    wpr = _lib.route_words_per_row(8300, 4)
+    assert wpr == 2
+    ok = torch.zeros(4 * wpr, dtype=torch.int32)
+    _lib._check_route_size(ok, 200, 8300, 4, None)
+    with pytest.raises(ValueError, match="kernel reads 8"):
+        _lib._check_route_size(ok[:-1], 200, 8300, 4, None)
+    # packed: at least ceil(T/64) rows
+    _lib._check_route_size(torch.zeros(130 * 2, dtype=torch.int32), 8300, 8300, 4,
+                           torch.tensor([0, 8300], dtype=torch.int32))
+    with pytest.raises(ValueError):
+        _lib._check_route_size(torch.zeros(129 * 2, dtype=torch.int32), 8300, 8300, 4,
+                               torch.tensor([0, 8300], dtype=torch.int32))

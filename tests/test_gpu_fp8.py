@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from test_gpu_parity import check, dev, gather, rand16, sample_rows, say, words_tensor
+from test_gpu_parity import block_rows, check, dev, gather, rand16, say, words_tensor
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -116,7 +116,7 @@ def test_fp8_workload_full_size(A, orc, name):
     q, k, v = W.draw_qkv(w)
     route = W.route_for(w)
     got = gpu_fp8(A, q, k, v, w.scale, w.causal, route=route, tpb=w.tiles_per_bit)
-    rows = sample_rows(np.random.default_rng(1234), w, 3)
+    rows = block_rows(np.random.default_rng(1234), w)
     ref = orc.attn_rows(q, k, v, rows, scale=w.scale, causal=w.causal, route=route, tiles_per_bit=w.tiles_per_bit,
                         lowp="fp8")
     mx, mn = check(gather(got, rows, False, None), ref, name)

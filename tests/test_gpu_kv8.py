@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from test_gpu_parity import MAX_ERR, MEAN_ERR, check, dev, gather, rand16, sample_rows, say, words_tensor
+from test_gpu_parity import MAX_ERR, MEAN_ERR, block_rows, check, dev, gather, rand16, say, words_tensor
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -155,9 +155,37 @@ def test_kv8_workload_full_size(A, orc, name):
     route = W.route_for(w)
     cu = W.cu_seqlens_of(w.seqlens) if w.varlen else None
     got = gpu_kv8(A, q, k8, sk, v8, sv, w.scale, w.causal, cu=cu, route=route, tpb=w.tiles_per_bit or 4)
-    rows = sample_rows(np.random.default_rng(1234), w, 6 if w.qsl <= 4096 else 3)
+    rows = block_rows(np.random.default_rng(1234), w)
     ref = orc.attn_rows_kv8(q, k8, sk, v8, sv, rows, scale=w.scale, causal=w.causal, cu_seqlens=cu, route=route,
                             tiles_per_bit=w.tiles_per_bit or 4)
     mx, mn = check(gather(got, rows, w.varlen, cu), ref, name)
     say("  rows %d max %.3g mean %.3g (bar %.0e / %.0e)" % (len(rows), mx, mn, MAX_ERR, MEAN_ERR))
     assert np.all(np.isfinite(got.astype(np.float32)))
+
+
+@pytest.mark.parametrize("vmul", [1e-3, 1e4])
+@pytest.mark.parametrize("routed", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_gpu_kv8_value_magnitudes(A, orc, vmul, routed, d, waves8):
+    """Value caches far from unit scale: values of order 1e-3 (their fp16
+    probabilities times v_scale would be fp16 subnormals if the scales were
+    applied as they are) and of order 1e4 with some rows at amax 6e4 (where
+    p * v_scale would overflow fp16 while p reaches 2^8 between rescales).
+    Checked relative to the value magnitude: |gpu - oracle| / vmul within the
+    usual bar."""
+    rng = np.random.default_rng(1700 + d + routed + int(np.log10(vmul)))
+    qsl, ksl = 150, 700
+    q = rand16(rng, (1, 8, qsl, d))
+    k = rand16(rng, (1, 2, ksl, d))
+    v = np.clip(rng.standard_normal((1, 2, ksl, d)) * vmul, -6.0e4, 6.0e4)
+    if vmul > 1:
+        v[0, :, ::37, 3] = 6.0e4          # rows at the top of the fp16 range
+    v = v.astype(np.float16)
+    k8, sk, v8, sv = encode(orc, k, v)
+    route = W.pack_bits(rng.random((3, W.n_route_groups(ksl, 2))) < 0.5) if routed else None
+    for causal in (False, True):
+        say("kv8 magnitude vmul=%g d=%d routed=%d causal=%d" % (vmul, d, routed, causal))
+        got = gpu_kv8(A, q, k8, sk, v8, sv, 0.1, causal, route=route, tpb=2)
+        assert np.all(np.isfinite(got.astype(np.float32)))
+        ref = orc.attn_fwd_kv8(q, k8, sk, v8, sv, scale=0.1, causal=causal, route=route, tiles_per_bit=2)
+        check(got.astype(np.float64) / vmul, ref / vmul, (vmul, causal))
