@@ -66,6 +66,8 @@ def load():
         lib.attn_debug_route_trace.restype = _I
         lib.attn_debug_check_cu_seqlens.argtypes = [_P, _I, _I]
         lib.attn_debug_check_cu_seqlens.restype = _I
+        lib.attn_fwd_noalloc_stream.argtypes = fwd_args + [_I, _P]
+        lib.attn_fwd_noalloc_stream.restype = _I
         _lib = lib
     return _lib
 
@@ -213,6 +215,16 @@ def attn_fwd_lowp_stream(q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, ca
                                        n_kvh, float(scale), int(bool(causal)), _ptr(cu_seqlens),
                                        _ptr(route_bitmask), int(tiles_per_bit), int(lowp_format),
                                        _stream(stream)))
+
+
+def attn_fwd_noalloc_stream(q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal,
+                            cu_seqlens=None, route_bitmask=None, tiles_per_bit=4, lowp_format=0, stream=None):
+    """Direct mirror of the allocation-free C entry point (static device
+    scratch, sizes passed explicitly)."""
+    _check(load().attn_fwd_noalloc_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, qsl, ksl, hdim, n_qh,
+                                          n_kvh, float(scale), int(bool(causal)), _ptr(cu_seqlens),
+                                          _ptr(route_bitmask), int(tiles_per_bit), int(lowp_format),
+                                          _stream(stream)))
 
 
 def attn_debug_quantize_rows(x, path=0, stream=None):

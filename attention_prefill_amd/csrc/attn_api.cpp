@@ -329,6 +329,32 @@ attn_status attn_debug_plan(int32_t B, int32_t qsl, int32_t ksl, int32_t hdim, i
     return ATTN_OK;
 }
 
+attn_status attn_fwd_noalloc_stream(const void* q, const void* k, const void* v, void* out, int32_t B,
+                                    int32_t qsl, int32_t ksl, int32_t hdim, int32_t n_qh, int32_t n_kvh,
+                                    float scale, int32_t causal, const int32_t* cu_seqlens,
+                                    const uint32_t* route_bitmask, int32_t tiles_per_bit, int32_t lowp_format,
+                                    void* hip_stream) {
+    attn::Problem p{q, k, v, out, B, qsl, ksl, hdim, n_qh, n_kvh, scale, causal != 0,
+                    cu_seqlens, route_bitmask, tiles_per_bit};
+    p.lowp = lowp_format;
+    attn_status vs = validate(p);
+    if (vs != ATTN_OK) return vs;
+    const size_t sbytes = attn::forward_scratch_bytes(p);
+    if (sbytes > attn::NOALLOC_SCRATCH_BYTES)
+        return fail(ATTN_ERR_SHAPE, "this call needs %zu bytes of scratch; the allocation-free entry point has %zu",
+                    sbytes, attn::NOALLOC_SCRATCH_BYTES);
+    void* scratch = nullptr;
+    hipError_t e = attn::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return hip_fail(e, "looking up the static scratch");
+    hipStream_t st = (hipStream_t)hip_stream;
+    e = attn::launch_forward(p, scratch, st);
+    if (e != hipSuccess) return hip_fail(e, "attention forward launch");
+    vs = debug_sync(st, "attention forward (ATTN_DEBUG_SYNC)");
+    if (vs != ATTN_OK) return vs;
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
 attn_status attn_debug_route_trace(const void* q, const void* k, const void* v, void* out, int32_t B,
                                    int32_t qsl, int32_t ksl, int32_t hdim, int32_t n_qh, int32_t n_kvh,
                                    float scale, int32_t causal, const int32_t* cu_seqlens,

@@ -35,6 +35,12 @@ struct Problem {
 // Device scratch a forward call needs (bytes): quantised K rows for routed
 // calls and split-key partials when the key range is split.  0 if none.
 size_t forward_scratch_bytes(const Problem& p);
+
+// The allocation-free entry point's device scratch: a static device array of
+// this many bytes per device; noalloc_scratch gives its address on the
+// current device (looked up once per device).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
 // The launch plan of a forward call (no device access): query wavefronts per
 // workgroup, key groups, heads per workgroup, rows per workgroup, workgroup
 // columns, row blocks per column, key splits, light-first pairing, grid size,

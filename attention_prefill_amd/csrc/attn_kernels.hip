@@ -47,9 +47,16 @@
 #include <stdlib.h>
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "attn_internal.h"
+
+// Device scratch of the allocation-free entry point (attn_fwd_noalloc_stream):
+// quantised K rows and split-key partials live here instead of in memory
+// allocated per call.  One copy per device, held from module load until the
+// process ends; every call on a device shares it.
+static __device__ __align__(256) char scratch[attn::NOALLOC_SCRATCH_BYTES];
 
 namespace attn {
 namespace {
@@ -1501,6 +1508,28 @@ static Plan make_plan(const Problem& p) {
 }
 
 size_t forward_scratch_bytes(const Problem& p) { return make_plan(p).bytes; }
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (host code never passes the array's own
+// name, a host-side stand-in, to the device).
+hipError_t noalloc_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 void forward_plan(const Problem& p, long long out[10]) {
     const Plan pl = make_plan(p);

@@ -183,6 +183,26 @@ attn_status attn_fwd_lowp_stream(const void* q, const void* k, const void* v, vo
                                  const int32_t* cu_seqlens, const uint32_t* route_bitmask,
                                  int32_t tiles_per_bit, int32_t lowp_format, void* hip_stream);
 
+/* attn_fwd_lowp_stream for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, kernels and result, but the scratch that
+ * routed calls (quantised K rows) and split-key calls (fp32 partials) need
+ * comes from a static device array of 64 MiB per device, held from library
+ * load until the process ends, instead of from the stream-ordered pool.  The
+ * call allocates nothing (no hipMalloc, hipFree or pool call).  A call whose
+ * scratch would exceed 64 MiB returns ATTN_ERR_SHAPE before any device work
+ * (for example routed calls over more than about 60 M key rows x hdim bytes).
+ * Every call on one device shares that array and nothing in it needs to
+ * start at zero: calls that overlap in time on one device (on different
+ * streams, or from different threads) race on it and must be serialised by
+ * the caller.  ATTN_DEBUG_VALIDATE is not applied here (it would allocate a
+ * host copy); ATTN_DEBUG_SYNC is. */
+attn_status attn_fwd_noalloc_stream(const void* q, const void* k, const void* v, void* out,
+                                    int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
+                                    int32_t n_qh, int32_t n_kvh, float scale, int32_t causal,
+                                    const int32_t* cu_seqlens, const uint32_t* route_bitmask,
+                                    int32_t tiles_per_bit, int32_t lowp_format, void* hip_stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none).
  * The string is owned by the library and valid until the next call. */
 const char* attn_last_error(void);

@@ -203,3 +203,18 @@ def test_binding_checks_bitmask_length(orc):
     with pytest.raises(ValueError):
         _lib._check_route_size(torch.zeros(129 * 2, dtype=torch.int32), 8300, 8300, 4,
                                torch.tensor([0, 8300], dtype=torch.int32))
+
+
+def test_noalloc_rejects_oversized_scratch():
+    """The allocation-free entry point: a routed call whose quantised K rows
+    alone exceed its 64 MiB static scratch returns ATTN_ERR_SHAPE before any
+    device work (fake pointers, never read)."""
+    lib = A.load()
+    # 8 kv heads x 65536 keys x (128 + 4) bytes = 69 MB of K codes and scales
+    st = lib.attn_fwd_noalloc_stream(FAKE, FAKE, FAKE, FAKE, 1, 64, 65536, 128, 8, 8, 0.1, 0, None, FAKE, 4, 0, None)
+    assert st == SHAPE and "scratch" in A.attn_last_error()
+    # the forward argument rules apply first
+    assert lib.attn_fwd_noalloc_stream(FAKE, FAKE, FAKE, None, 1, 64, 64, 64, 4, 2, 0.1, 0, None, None, 4, 0,
+                                       None) == NULL
+    assert lib.attn_fwd_noalloc_stream(FAKE, FAKE, FAKE, FAKE, 1, 64, 64, 64, 4, 2, 0.1, 0, None, FAKE, 4, 7,
+                                       None) == ARG
