@@ -9,7 +9,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libattn_mi355x.so")
+# ATTN_LIB_PATH selects another build of the same library (for instance one
+# compiled with a build-time alternative, for A/B timing)
+LIB_PATH = os.environ.get("ATTN_LIB_PATH") or os.path.join(PKG, "libattn_mi355x.so")
 
 ATTN_OK = 0
 STATUS_NAMES = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",

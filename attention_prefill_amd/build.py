@@ -19,13 +19,15 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the library to `out`; `defines` are extra -D settings of the
+    kernel source (build-time alternatives such as ATTN_FUSED_KQUANT=1)."""
     objs, procs = [], []
-    bdir = os.path.join(PKG, "_build")
+    bdir = os.path.join(PKG, "_build" if not defines else "_build_" + "_".join(d.replace("=", "") for d in defines))
     os.makedirs(bdir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(bdir, src + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *("-D" + d for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append(subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True))
@@ -40,11 +42,11 @@ def build(verbose: bool = False) -> str:
         failed |= p.returncode != 0
     if failed:
         raise RuntimeError("hipcc failed")
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
                     "-L/opt/rocm/lib", "-lrocblas"], check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -84,6 +84,14 @@ constexpr int NKB = BN / 32;        // 32-key score blocks per tile
 #ifndef ATTN_STAGES4
 #define ATTN_STAGES4 1
 #endif
+// Where routed calls quantise their K rows: 0 = once per call in a pass of
+// their own (quantize_rows_kernel) whose codes the low-precision tiles load;
+// 1 = in the tile loader of every workgroup, from the fp16 K tile, as it is
+// staged into LDS (the same device rounding, so the same codes).  Both are
+// built and timed; 0 is the default (measured faster).
+#ifndef ATTN_FUSED_KQUANT
+#define ATTN_FUSED_KQUANT 0
+#endif
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RNE_MAGIC = 12582912.0f;   // 1.5 * 2^23
 // dword 3 of a raw buffer descriptor (32-bit data format, no swizzle, no
@@ -531,7 +539,7 @@ void attn_fwd_kernel(FwdArgs a) {
         u32x4(&kreg)[KCH] = sg.kreg;
         u32x4(&vreg)[VB][4] = sg.vreg;
         u32x4& skreg = sg.skreg;
-        if (KV8 || (ROUTED && i8)) {
+        if (KV8 || (ROUTED && i8 && !ATTN_FUSED_KQUANT)) {
             const __amdgpu_buffer_rsrc_t k8rs = tile_rsrc(k8b, Lk * HD, TB8, kt);
 #pragma unroll
             for (int n = 0; n < K8CH; ++n) {
@@ -595,9 +603,45 @@ void attn_fwd_kernel(FwdArgs a) {
         char* kbuf = smem + (stage * KS + kgp) * L::STAGE;
         _Float16* vt = (_Float16*)(kbuf + L::KREG);
         float* scl = (float*)(kbuf + L::KREG + L::VBYTES);
-        if ((KV8 || (ROUTED && i8)) && tid < BN / 4)
+        if ((KV8 || (ROUTED && i8 && !ATTN_FUSED_KQUANT)) && tid < BN / 4)
             *(f32x4*)(scl + 4 * tid) = __builtin_bit_cast(f32x4, skreg) * a.c;
-        if (ROUTED && i8) {
+        if (ROUTED && i8 && !KV8 && ATTN_FUSED_KQUANT) {
+            // the fp16 K tile quantised here: the HD/8 consecutive lanes that
+            // hold one row share its absolute maximum, then each codes its 8
+            // values with the rule of the per-call pass (same functions)
+#pragma unroll
+            for (int n = 0; n < KCH; ++n) {
+                const int c = tid + n * NT;
+                const int row = c / (HD / 8);
+                const int part = c % (HD / 8);
+                const f16x8 xv = __builtin_bit_cast(f16x8, kreg[n]);
+                float amax = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf((float)xv[j]));
+#pragma unroll
+                for (int o = 1; o < HD / 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+                float sc, inv;
+                unsigned w0 = 0, w1 = 0;
+                if constexpr (FP8) {
+                    fp8_scale(amax, sc, inv);
+                    w0 = fp8_pack4(fp8_round((float)xv[0], inv), fp8_round((float)xv[1], inv),
+                                   fp8_round((float)xv[2], inv), fp8_round((float)xv[3], inv));
+                    w1 = fp8_pack4(fp8_round((float)xv[4], inv), fp8_round((float)xv[5], inv),
+                                   fp8_round((float)xv[6], inv), fp8_round((float)xv[7], inv));
+                } else {
+                    quant_scale(amax, sc, inv);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        w0 |= ((unsigned)quant_code((float)xv[j], inv) & 0xffu) << (8 * j);
+                        w1 |= ((unsigned)quant_code((float)xv[4 + j], inv) & 0xffu) << (8 * j);
+                    }
+                }
+                if (KTOT % NT == 0 || c < KTOT) {
+                    *(u32x2*)(kbuf + row * L::K8P + part * 8) = u32x2{w0, w1};
+                    if (part == 0) scl[row] = sc * a.c;
+                }
+            }
+        } else if (ROUTED && i8) {
 #pragma unroll
             for (int n = 0; n < K8CH; ++n) {
                 const int c = tid + n * NT;
@@ -1490,7 +1534,7 @@ static Plan make_plan(const Problem& p) {
         pl.pair_blocks = (force_pair[0] == '1' && p.causal && !varlen) ? 1 : 0;
     pl.out_rows = varlen ? (long long)p.n_qh * p.qsl : (long long)p.B * p.n_qh * p.qsl;
     size_t off = 0;
-    if (routed && !kv8) {
+    if (routed && !kv8 && !ATTN_FUSED_KQUANT) {
         const size_t krows = varlen ? (size_t)p.n_kvh * p.ksl : (size_t)p.B * p.n_kvh * p.ksl;
         pl.k8_off = off;
         off += round_up(krows * p.hdim);
@@ -1585,7 +1629,7 @@ hipError_t launch_forward(const Problem& p, void* scratch, hipStream_t st) {
         const int n_kt = (p.ksl + TK - 1) / TK;
         const int n_g = (n_kt + p.tiles_per_bit - 1) / p.tiles_per_bit;
         a.wpr = (n_g + 31) / 32;
-        if (!kv8) {
+        if (!kv8 && !ATTN_FUSED_KQUANT) {
             // INT8 codes of every K row, once per call (a cache brings its own)
             const size_t krows = varlen ? (size_t)p.n_kvh * p.ksl : (size_t)p.B * p.n_kvh * p.ksl;
             a.k8 = (const int8_t*)((char*)scratch + pl.k8_off);
