@@ -19,15 +19,26 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+# host code only, for the CPU sanitizer run of the host-side tests: AddressSanitizer
+# and UndefinedBehaviorSanitizer (errors fatal); device code is built as usual
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g"]
+
+
+def build(verbose: bool = False, out: str = LIB, defines=(), sanitize_host: bool = False) -> str:
     """Compile the library to `out`; `defines` are extra -D settings of the
-    kernel source (build-time alternatives such as ATTN_FUSED_KQUANT=1)."""
+    kernel source (build-time alternatives such as ATTN_FUSED_KQUANT=1);
+    sanitize_host instruments the host code (the result then needs the
+    sanitizer runtime preloaded)."""
     objs, procs = [], []
-    bdir = os.path.join(PKG, "_build" if not defines else "_build_" + "_".join(d.replace("=", "") for d in defines))
+    tag = "_".join(d.replace("=", "") for d in defines) + ("_san" if sanitize_host else "")
+    bdir = os.path.join(PKG, "_build" if not tag else "_build_" + tag)
     os.makedirs(bdir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(bdir, src + ".o")
-        cmd = [HIPCC, *FLAGS, *("-D" + d for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *(HOST_SANITIZE if sanitize_host else []), *("-D" + d for d in defines), "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append(subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True))

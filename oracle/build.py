@@ -10,17 +10,28 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build_oracle(force: bool = True) -> str:
+# the LLVM C compiler of the ROCm install (its sanitizer runtime is the one the
+# HIP library's host code links against, so both share one runtime)
+CLANG = "/opt/rocm/llvm/bin/clang"
+
+
+def build_oracle(force: bool = True, out: str = LIB, sanitize: bool = False) -> str:
+    """gcc with OpenMP by default; with sanitize, clang with AddressSanitizer
+    and UndefinedBehaviorSanitizer (errors fatal) and no OpenMP."""
     src = os.path.join(HERE, "oracle.c")
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(src):
-        return LIB
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
-           "-ffp-contract=off", "-fno-fast-math", "-frounding-math",
-           "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    common = ["-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-frounding-math", "-Wall",
+              "-Wextra"]
+    if sanitize:
+        cmd = [CLANG, "-O1", "-g", *common, "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+               "-fno-omit-frame-pointer", "-o", tmp, src, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", *common, "-fopenmp", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

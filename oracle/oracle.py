@@ -22,9 +22,14 @@ _I = ctypes.c_int
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build_oracle(force=False)
-        lib = ctypes.CDLL(_build.LIB)
+        # ORACLE_LIB_PATH selects another build of oracle.c (the sanitizer
+        # build of the CPU test run)
+        path = os.environ.get("ORACLE_LIB_PATH")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build_oracle(force=False)
+        lib = ctypes.CDLL(path)
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = ctypes.c_double
         lib.oracle_f64_to_f16_rne.argtypes = [ctypes.c_double]
