@@ -60,7 +60,7 @@ for _n in W.WORKLOADS:
     BENCH_SETS.setdefault(_n, [_n])
 
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
-KERNEL_SOURCE = os.path.join(ROOT, "attention_prefill_amd", "csrc", "attn_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "attention_prefill_amd", "csrc", f) for f in ("attn_kernels.hip", "attn_device.h")]
 
 
 def parse():
@@ -236,6 +236,15 @@ def int8_share(w, route):
     return low / tot if tot else 0.0
 
 
+def kernel_source_sha256():
+    """sha256 over the kernel sources (attn_kernels.hip, then attn_device.h)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def hbm_traffic(workload, dominant_name):
     """HBM bytes per launch of the dominant kernel of this workload from the
     committed counter summary, or None when the counters were not taken on
@@ -243,8 +252,7 @@ def hbm_traffic(workload, dominant_name):
     try:
         with open(COUNTERS_FILE) as f:
             rec = json.load(f)
-        with open(KERNEL_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_sha256()
         if rec.get("kernel_source_sha256") != sha:
             return None
         ent = rec["workloads"].get(workload, {}).get(dominant_name)
