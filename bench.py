@@ -418,15 +418,22 @@ def main():
     if vs is not None:
         rec["vs_baseline_note"] = "the page's fused time for these shapes; its hardware is not stated"
     if any(c.route is not None for c in calls) and not args.no_compare:
-        # the all-FP16 run of the same inputs: the same kernel with a zero
-        # bitmask, and for context the dense kernel with no bitmask at all
-        zero_step = time_route("zero")
-        dense_step = time_route("none")
-        rec["all_fp16_ms_per_step"] = round(zero_step * 1e3, 5)
-        rec["all_fp16_tflops"] = round(metric_flop / zero_step / 1e12, 3)
-        rec["routed_speedup_vs_all_fp16"] = round(zero_step / sec_per_step, 4)
-        rec["dense_no_bitmask_ms_per_step"] = round(dense_step * 1e3, 5)
-        rec["routed_speedup_vs_dense"] = round(dense_step / sec_per_step, 4)
+        # the all-FP16 run of the same inputs (the same kernel with a zero
+        # bitmask) and, for context, the dense kernel with no bitmask at all;
+        # the three are timed in interleaved rounds (K steps each, medians
+        # over the rounds), so that clock drift over the run does not favour
+        # whichever runs first
+        rounds = {"drawn": [], "zero": [], "none": []}
+        for _ in range(3):
+            for r in rounds:
+                rounds[r].append(time_route(r))
+        med = {r: float(np.median(v)) for r, v in rounds.items()}
+        rec["all_fp16_ms_per_step"] = round(med["zero"] * 1e3, 5)
+        rec["all_fp16_tflops"] = round(metric_flop / med["zero"] / 1e12, 3)
+        rec["routed_ms_per_step_interleaved"] = round(med["drawn"] * 1e3, 5)
+        rec["routed_speedup_vs_all_fp16"] = round(med["zero"] / med["drawn"], 4)
+        rec["dense_no_bitmask_ms_per_step"] = round(med["none"] * 1e3, 5)
+        rec["routed_speedup_vs_dense"] = round(med["none"] / med["drawn"], 4)
     if args.fp16_compare and any(c.w.kv8 for c in calls):
         # the same call on the fp16 K and V the cache was encoded from
         kv16_step = time_route("drawn", fp16_kv=True)
