@@ -73,6 +73,8 @@ def parse():
                          "passed, so that the GPU clock has reached its sustained level (0: none)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(BENCH_SETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the CPU oracle baseline (default: the process's CPUs, or OMP_NUM_THREADS)")
     ap.add_argument("--no-compare", action="store_true",
                     help="skip the all-FP16 and dense runs of a routed workload (for profiler runs whose "
                          "per-kernel averages must cover the drawn bitmask only)")
@@ -163,14 +165,14 @@ def host_cpu():
     return os.cpu_count() or 1, allowed, model
 
 
-def cpu_baseline(calls, budget_s=12.0):
+def cpu_baseline(calls, budget_s=12.0, threads=0):
     """The oracle, untuned, on a bounded sample: whole query heads of each call
     (full sequence length, the same inputs), as many as fit the time budget.
-    Threads: every CPU this process may run on, or OMP_NUM_THREADS when the
-    host sets it (the GPU's share of a shared host)."""
+    Threads: `threads` if given, else every CPU this process may run on, or
+    OMP_NUM_THREADS when the host sets it (the GPU's share of a shared host)."""
     import oracle
     nproc, allowed, model = host_cpu()
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or allowed
+    threads = threads or int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or allowed
     flop = secs = 0.0
     samples = []
     for c in calls:
@@ -454,7 +456,7 @@ def main():
         rec["unfused_ms_per_step"] = round(unf_step * 1e3, 5)
         rec["fused_speedup_vs_unfused"] = round(unf_step / sec_per_step, 3)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(calls)
+        rec["cpu_baseline"] = cpu_baseline(calls, threads=args.cpu_threads)
     print(json.dumps(rec), flush=True)
 
 
