@@ -192,6 +192,45 @@ __device__ __forceinline__ void quantize_q_regs(const f16x8 (&qf)[HD / 16], i32x
 // Exact int8 -> fp16 of the four signed bytes of w: with u = b + 128 in the low
 // byte and 0x64 above it, a 16-bit lane holds the fp16 value 1024 + u, and
 // subtracting 1152 leaves b.  Lanes hold bytes 0,1 (first word), 2,3 (second).
+// A pointer into LDS (address space 3), for the builtins that take one.
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Transposed 8-byte LDS reads (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane 4a + b receives as element j the element b of the four
+// 16-bit values that lane 4j + a addresses.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(size_t)LDS_PTR(const char, p);
+}
+
+// Four 8-key operand fragments from transposed reads: fragment i takes the
+// two reads at LDS byte address a_i and a_i + 1024 (its keys 0-3 and 4-7 of
+// a row-major [key][d] tile with 256-byte rows).  The reads and the wait for
+// them are one asm block: written with the builtin, every such read would be
+// made to wait for all direct tile loads in flight, which the compiler
+// cannot tell apart from it; the barrier protocol of the callers already
+// orders these reads after the loads of their stage.
+__device__ __forceinline__ void lds_read_tr16_x4(unsigned a0, unsigned a1, unsigned a2, unsigned a3,
+                                                 f16x8 (&f)[4]) {
+    f16x4 r0, r1, r2, r3, r4, r5, r6, r7;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %6, %11\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+    f[0] = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+    f[1] = __builtin_shufflevector(r2, r3, 0, 1, 2, 3, 4, 5, 6, 7);
+    f[2] = __builtin_shufflevector(r4, r5, 0, 1, 2, 3, 4, 5, 6, 7);
+    f[3] = __builtin_shufflevector(r6, r7, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 __device__ __forceinline__ u32x2 widen_i8x4(unsigned w) {
     const unsigned u = w ^ 0x80808080u;
     const f16x2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};

@@ -79,6 +79,13 @@ constexpr int NKB = BN / 32;        // 32-key score blocks per tile
 #ifndef ATTN_FUSED_KQUANT
 #define ATTN_FUSED_KQUANT 0
 #endif
+// Tile loads of the hdim-128 four-stage kernels (fp16 K and V, INT8 or FP8
+// K codes and their scales): 1 = buffer loads that write LDS directly (no
+// staging registers, no LDS store instructions, no transpose work on the
+// VALU); 0 = loads into registers and LDS stores, as the other kernels.
+#ifndef ATTN_DMA
+#define ATTN_DMA 1
+#endif
 // ---------------------------------------------------------------------------
 // LDS layout of one stage: the K tile (fp16 [key][d], or INT8 codes
 // [key][d]), the V tile stored transposed, [d][key], so that the P.V operand
@@ -93,6 +100,30 @@ constexpr int NKB = BN / 32;        // 32-key score blocks per tile
 __host__ __device__ constexpr int n_stages(int nw, int ks, bool routed) {
     return (ATTN_STAGES4 && nw == 8 && ks == 1) ? 4 : 2;
 }
+// Kernel shapes whose tiles travel from global memory to LDS directly.
+__host__ __device__ constexpr bool use_dma(int hd, int nw, int ks, bool routed, bool kv8) {
+    return ATTN_DMA && !ATTN_FUSED_KQUANT && BN == 64 && hd == 128 && !kv8 && n_stages(nw, ks, routed) == 4;
+}
+
+// Directly loaded stages are unpadded and row-major, with the 16-byte
+// chunks of each row permuted by an XOR of the row index, so that the
+// operand reads of 16 lanes (16-byte reads) or 32 lanes (8-byte transposed
+// reads), all at one column of different rows, fall on distinct banks:
+// - fp16 K, 16 chunks per row: chunk c of row r at c ^ (r & 15);
+// - INT8 / FP8 K codes, 8 chunks per 128-byte row (two rows per bank
+//   sweep): chunk c of row r at c ^ ((r >> 1) & 7);
+// - V, [key][d], 16 chunks per row, read four keys by 4 x 4 d at a time:
+//   chunk c of key r at c ^ (4 * (r & 3)).
+// The per-key scales of a tile follow the V tile (raw s_k, then s_v).
+template <int HD>
+struct LdsDma {
+    static constexpr int KBYTES = BN * HD * 2;
+    static constexpr int KREG = KBYTES;
+    static constexpr int VBYTES = BN * HD * 2;
+    static constexpr int SCL = 2 * BN * 4;
+    static constexpr int STAGE = KREG + VBYTES + SCL;
+    static constexpr int TOTAL = 2 * STAGE;
+};
 
 template <int HD>
 struct Lds {
@@ -129,6 +160,12 @@ void attn_fwd_kernel(FwdArgs a) {
     constexpr int PF = (HD == 64 && !ROUTED && !KV8 && NW == 4 && BN == 64) ? 2 : 1;
     // four LDS stages and tiles stored two ahead: a barrier every other tile
     constexpr int NST = n_stages(NW, KS, ROUTED);
+    // tiles loaded straight into LDS (layout: LdsDma)
+    constexpr bool DMA = use_dma(HD, NW, KS, ROUTED, KV8);
+    static_assert(!DMA || (NW == 8 && KS == 1 && HD == 128 && BN == 64 && NST == 4), "direct-load shape");
+    constexpr int STG = DMA ? LdsDma<HD>::STAGE : L::STAGE;     // bytes of one stage
+    constexpr int KRG = DMA ? LdsDma<HD>::KREG : L::KREG;       // V tile offset in a stage
+    constexpr int VBY = DMA ? LdsDma<HD>::VBYTES : L::VBYTES;   // scales follow the V tile
     // Request all of a tile's K and V fragments before its first MFMA (the
     // hdim-64 kernel has the registers for them).
     constexpr bool EARLY = (HD == 64);
@@ -282,7 +319,7 @@ void attn_fwd_kernel(FwdArgs a) {
             sg.r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs2, voff2[i], 0, 0));
     };
     auto lstore2 = [&](const Staging2& sg, int stage) __attribute__((always_inline)) {
-        char* kbuf = smem + (stage * KS + kgp) * L::STAGE;
+        char* kbuf = smem + (stage * KS + kgp) * STG;
         if (v_half) {
             _Float16* vt = (_Float16*)(kbuf + L::KREG);
             const int kg = th % (BN / 4), dc = th / (BN / 4);
@@ -371,7 +408,7 @@ void attn_fwd_kernel(FwdArgs a) {
         const u32x4(&kreg)[KCH] = sg.kreg;
         const u32x4(&vreg)[VB][4] = sg.vreg;
         const u32x4& skreg = sg.skreg;
-        char* kbuf = smem + (stage * KS + kgp) * L::STAGE;
+        char* kbuf = smem + (stage * KS + kgp) * STG;
         _Float16* vt = (_Float16*)(kbuf + L::KREG);
         float* scl = (float*)(kbuf + L::KREG + L::VBYTES);
         if ((KV8 || (ROUTED && i8 && !ATTN_FUSED_KQUANT)) && tid < BN / 4)
@@ -480,6 +517,53 @@ void attn_fwd_kernel(FwdArgs a) {
             *(f32x4*)(scl + BN + 4 * (tid - BN / 4)) = __builtin_bit_cast(f32x4, sg.svreg) * vfac;
     };
 
+    // Direct tile loads (DMA kernels): each wavefront writes whole 1 KB LDS
+    // blocks, 64 lanes x 16 bytes in lane order; each lane fetches the global
+    // chunk that the swizzled layout puts at its slot.  fp16 K and V: 16
+    // blocks of 4 rows each, two per wavefront; INT8/FP8 codes: 8 blocks of 8
+    // rows, one per wavefront, and the 64 key scales (4 bytes a lane) by
+    // wavefront 0.  Reads past the sequence end return zeros, as above.
+    auto dma = [&](int kt, int stage, bool i8) __attribute__((always_inline)) {
+        if constexpr (DMA) {
+            char* base = smem + stage * STG;
+            if (ROUTED && i8) {
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(k8b, Lk * HD, TB8, kt);
+                const int row = 8 * w + (l >> 3);
+                const int c = (l & 7) ^ ((row >> 1) & 7);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, base + w * 1024), 16, row * HD + c * 16,
+                                                         0, 0, 0);
+                if (w == 0) {
+                    const __amdgpu_buffer_rsrc_t ss = tile_rsrc(skb, Lk * 4, TBS, kt);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ss, LDS_PTR(void, base + KRG + VBY), 4, l * 4, 0, 0, 0);
+                }
+            } else {
+                const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kb, slab, TB16, kt);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int blk = 2 * w + i;
+                    const int row = 4 * blk + (l >> 4);
+                    const int c = (l & 15) ^ (row & 15);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, base + blk * 1024), 16,
+                                                             row * (HD * 2) + c * 16, 0, 0, 0);
+                }
+            }
+            const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vb, slab, TB16, kt);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int blk = 2 * w + i;
+                const int row = 4 * blk + (l >> 4);
+                const int c = (l & 15) ^ (4 * (row & 3));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, base + KRG + blk * 1024), 16,
+                                                         row * (HD * 2) + c * 16, 0, 0, 0);
+            }
+        }
+    };
+    // every wave's direct loads complete, then the barrier
+    auto dsync = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
     // ---- state --------------------------------------------------------------------
     f32x16 o[NDB];
 #pragma unroll
@@ -489,17 +573,38 @@ void attn_fwd_kernel(FwdArgs a) {
 
     // K row read by this lane for the score A operand: bits 2 and 3 swapped
     const int krow = (lq & ~12) | ((lq & 4) << 1) | ((lq & 8) >> 1);
+    // Operand read offsets in a directly loaded stage (swizzles of LdsDma):
+    // koff[t]: the fp16 K fragment of d-step t (chunk 2g + 4(t/2) + t%2) of
+    // row krow; k8off[j]: the 16-byte code chunk g + 2j of row krow; voff[db]:
+    // this lane's 8-byte source of the transposed V reads of d block db,
+    // key 8*(l/32) + (l%16)/4 (+4 for the second read), d 32db + 16*((l/16)%2)
+    // + 4*(l%4): within 16 lanes, transposed lane 4a + b takes element b of
+    // source lane 4j + a as its element j, so lane l ends up with d = l % 32
+    // and the 4 consecutive keys of each read.
+    int koff[DMA ? HD / 16 : 1], k8off[DMA ? HD / 32 : 1], voff[DMA ? NDB : 1];
+    if constexpr (DMA) {
+#pragma unroll
+        for (int t = 0; t < HD / 16; ++t)
+            koff[t] = krow * (HD * 2) + (((2 * g + 4 * (t / 2) + (t % 2)) ^ (krow & 15)) << 4);
+#pragma unroll
+        for (int j = 0; j < HD / 32; ++j) k8off[j] = krow * HD + (((g + 2 * j) ^ ((krow >> 1) & 7)) << 4);
+        const int q4 = (l >> 2) & 3;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            voff[db] = (8 * (l >> 5) + q4) * (HD * 2) +
+                       ((4 * (db ^ q4) + 2 * ((l >> 4) & 1) + ((l & 3) >> 1)) << 4) + 8 * (l & 1);
+    }
 
     // One key tile: scores, optional mask, online softmax, P.V.
     auto tile = [&](auto mask_tag, int stage, int kt, bool i8) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const char* kbuf = smem + (stage * KS + kgp) * L::STAGE;
-        const _Float16* vt = (const _Float16*)(kbuf + L::KREG);
+        const char* kbuf = smem + (stage * KS + kgp) * STG;
+        const _Float16* vt = (const _Float16*)(kbuf + KRG);
         float x[NKB][16];
         float amul;
         f16x8 vfr[EARLY ? 2 * NKB : 1][EARLY ? NDB : 1];   // V fragments requested with K
         // per-key scales of the tile (INT8 tiles, key/value caches)
-        const float* skc = (const float*)(kbuf + L::KREG + L::VBYTES);
+        const float* skc = (const float*)(kbuf + KRG + VBY);
         const float* svc = skc + BN;
         // x[kb32][i] *= the scale of its key: this lane's keys are
         // 32*kb32 + 8*g + (i%8) + 16*(i/8)
@@ -524,10 +629,12 @@ void attn_fwd_kernel(FwdArgs a) {
             for (int kb32 = 0; kb32 < NKB; ++kb32) {
                 f32x16 acc = f32x16{};
                 const int8_t* kr = (const int8_t*)kbuf + (32 * kb32 + krow) * L::K8P + 16 * g;
+                const char* kd = kbuf + 32 * kb32 * HD;
 #pragma unroll
                 for (int k2 = 0; k2 < HD / 64; ++k2) {
-                    const i32x4 a0 = *(const i32x4*)(kr + 64 * k2);
-                    const i32x4 a1 = *(const i32x4*)(kr + 64 * k2 + 32);
+                    const i32x4 a0 = DMA ? *(const i32x4*)(kd + k8off[DMA ? 2 * k2 : 0]) : *(const i32x4*)(kr + 64 * k2);
+                    const i32x4 a1 = DMA ? *(const i32x4*)(kd + k8off[DMA ? 2 * k2 + 1 : 0])
+                                         : *(const i32x4*)(kr + 64 * k2 + 32);
                     const i32x8 av = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
                     const i32x4 b0 = q8[2 * k2], b1 = q8[2 * k2 + 1];
                     const i32x8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
@@ -537,22 +644,25 @@ void attn_fwd_kernel(FwdArgs a) {
                 for (int i = 0; i < 16; ++i) x[kb32][i] = acc[i];
                 key_scale(kb32);
             }
-            amul = sq_mul;
+            // direct loads keep the raw key scales: |scale|*log2(e) joins sq here
+            amul = DMA ? sq_mul * a.c : sq_mul;
         } else if (ROUTED && i8) {
 #pragma unroll
             for (int kb32 = 0; kb32 < NKB; ++kb32) {
                 i32x16 acc = i32x16{};
                 const int8_t* kr = (const int8_t*)kbuf + (32 * kb32 + krow) * L::K8P + 16 * g;
+                const char* kd = kbuf + 32 * kb32 * HD;
 #pragma unroll
                 for (int ks = 0; ks < HD / 32; ++ks) {
-                    i32x4 av = *(const i32x4*)(kr + 32 * ks);
+                    i32x4 av = DMA ? *(const i32x4*)(kd + k8off[DMA ? ks : 0]) : *(const i32x4*)(kr + 32 * ks);
                     acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, q8[ks], acc, 0, 0, 0);
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) x[kb32][i] = (float)acc[i];
                 key_scale(kb32);
             }
-            amul = sq_mul;
+            // direct loads keep the raw key scales: |scale|*log2(e) joins sq here
+            amul = DMA ? sq_mul * a.c : sq_mul;
         } else {
             const _Float16* k16 = (const _Float16*)kbuf;
             if constexpr (EARLY) {
@@ -587,9 +697,11 @@ void attn_fwd_kernel(FwdArgs a) {
                 for (int kb32 = 0; kb32 < NKB; ++kb32) {
                     f32x16 acc = f32x16{};
                     const _Float16* kr = k16 + (32 * kb32 + krow) * L::KP + 16 * g;
+                    const char* kd = kbuf + 32 * kb32 * (HD * 2);
 #pragma unroll
                     for (int t = 0; t < HD / 16; ++t) {
-                        const f16x8 av = *(const f16x8*)(kr + 32 * (t / 2) + 8 * (t % 2));
+                        const f16x8 av = DMA ? *(const f16x8*)(kd + koff[DMA ? t : 0])
+                                             : *(const f16x8*)(kr + 32 * (t / 2) + 8 * (t % 2));
                         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, qf[t], acc, 0, 0, 0);
                     }
 #pragma unroll
@@ -620,14 +732,26 @@ void attn_fwd_kernel(FwdArgs a) {
         const _Float16* vrow = vt + lq * L::VTP + 8 * g;
         auto pv = [&](int kb32, const f16x8(&pkb)[2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
+                const int kk = 2 * kb32 + t;
+                if constexpr (DMA) {
+                    // keys 16kk + 8(l/32) + 0..7 of d = 32db + l%32, every db
+                    const unsigned va = lds_addr(vt) + kk * 16 * (HD * 2);
+                    f16x8 fr[4];
+                    lds_read_tr16_x4(va + voff[0], va + voff[DMA ? 1 : 0], va + voff[DMA ? 2 : 0],
+                                     va + voff[DMA ? 3 : 0], fr);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int kk = 2 * kb32 + t;
-                    const f16x8 av = (EARLY && !(ROUTED && i8)) ? vfr[kk][db]
-                                                                 : *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pkb[t], o[db], 0, 0, 0);
+                    for (int db = 0; db < NDB; ++db)
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[db], pkb[t], o[db], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const f16x8 av = (EARLY && !(ROUTED && i8)) ? vfr[kk][db]
+                                                                     : *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pkb[t], o[db], 0, 0, 0);
+                    }
                 }
+            }
         };
 
         // online softmax in base 2 with a lazily moved reference max
@@ -734,6 +858,70 @@ void attn_fwd_kernel(FwdArgs a) {
         auto next_of = [&](int t, bool c) __attribute__((always_inline)) { return cur.next(t, c); };
         // test hook: count every tile the workgroup visits, by route
         uint32_t* const trace = a.trace ? a.trace + (size_t)(rrow0 + m0 / TQ) * a.trace_nkt : nullptr;
+        if constexpr (DMA) {
+        // Direct loads: each pass starts in stage 0 with its first tile
+        // resident and its second in flight, and loads the tile two ahead of
+        // the one it computes into the stage freed two steps before.  The
+        // steps of fully visible tiles are unrolled by four so that every
+        // stage offset is a constant: the compiler then sees that the loads
+        // in flight write other stages than the one read and waits for them
+        // only at the barriers.  The last (masked) tiles of a pass use a
+        // computed stage.
+        auto dpass = [&](auto cls_tag, int kt) __attribute__((always_inline)) {
+            constexpr bool C = decltype(cls_tag)::value;
+            int kn = next_of(kt + 1, C);
+            int kn2 = kn < kt1 ? next_of(kn + 1, C) : kt1;
+            auto step = [&](auto mask_tag, int S) __attribute__((always_inline)) {
+                constexpr bool MASK = decltype(mask_tag)::value;
+                if (trace && tid == 0) atomicAdd(trace + kt, C ? 0x10000u : 1u);
+                if (kn2 < kt1) dma(kn2, (S + 2) & 3, C);
+                if (MASK ? kt < kt_end : wave_active) tile(mask_tag, S, kt, C);
+                if (S & 1) dsync();
+                kt = kn;
+                kn = kn2;
+                if (kn2 < kt1) kn2 = next_of(kn2 + 1, C);
+            };
+            const int full_end = min(nfull, kt1);
+            int si = 0;
+            while (true) {
+                if (kt >= full_end) break;
+                step(std::false_type{}, 0);
+                si = 1;
+                if (kt >= full_end) break;
+                step(std::false_type{}, 1);
+                si = 2;
+                if (kt >= full_end) break;
+                step(std::false_type{}, 2);
+                si = 3;
+                if (kt >= full_end) break;
+                step(std::false_type{}, 3);
+                si = 0;
+            }
+            while (kt < kt1) {
+                step(std::true_type{}, si);
+                si = (si + 1) & 3;
+            }
+            dsync();
+        };
+        int kt = next_of(kt0, false);
+        int kt2 = kt < kt1 ? next_of(kt + 1, false) : kt1;
+        if (kt < kt1) dma(kt, 0, false);
+        if (kt2 < kt1) dma(kt2, 1, false);
+        query_prologue();
+        dsync();
+        dpass(std::false_type{}, kt);
+        kt = next_of(kt0, true);
+        kt2 = kt < kt1 ? next_of(kt + 1, true) : kt1;
+        if (kt < kt1) {
+            dma(kt, 0, true);
+            if (kt2 < kt1) dma(kt2, 1, true);
+            float sq;
+            quantize_q_regs<HD, FP8>(qf, q8, sq);
+            sq_mul = sq > 0.0f ? sq : 1.0f;
+            dsync();
+            dpass(std::true_type{}, kt);
+        }
+        } else {
         int st = 0;
         // tiles [kt, kt1) of route C: the first (kt) already in LDS stage st
         // and, with four stages, the second in stage st+1; with four stages
@@ -810,6 +998,36 @@ void attn_fwd_kernel(FwdArgs a) {
             __syncthreads();
             pass(std::true_type{}, kt);
         }
+        }
+    } else if constexpr (DMA) {
+    // Direct loads (one key group): tiles 0 and 1 in stages 0 and 1; step it
+    // loads tile it + 2 into the stage step it - 2 read, computes tile it
+    // and, after odd steps, waits for its loads and meets the barrier.  Fully
+    // visible tiles run unrolled by four with constant stage offsets (see the
+    // routed passes), the masked tail with a computed stage.
+    if (has(0)) dma(kt_first, 0, false);
+    if (has(1)) dma(kt_first + 1, 1, false);
+    query_prologue();
+    dsync();
+    auto dstep = [&](auto mask_tag, int S, int it) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int kt = kt_first + it;
+        if (has(it + 2)) dma(kt + 2, (S + 2) & 3, false);
+        if (MASK ? kt < kt_end : wave_active) tile(mask_tag, S, kt, false);
+        if (S & 1) dsync();
+    };
+    int it = 0;
+    while (true) {
+        if (it >= it_full) break;
+        dstep(std::false_type{}, 0, it++);
+        if (it >= it_full) break;
+        dstep(std::false_type{}, 1, it++);
+        if (it >= it_full) break;
+        dstep(std::false_type{}, 2, it++);
+        if (it >= it_full) break;
+        dstep(std::false_type{}, 3, it++);
+    }
+    for (; it < n_it; ++it) dstep(std::true_type{}, it & 3, it);
     } else {
     // Prologue: the first PF tiles' loads go out behind the query loads, and
     // one wait covers them all.
@@ -1094,7 +1312,8 @@ hipError_t set_lds(K kernel, int bytes) {
 template <int HD, int NW, int KS, bool CAUSAL, bool VARLEN, bool ROUTED, bool KV8, bool FP8>
 hipError_t launch_fwd_t(const FwdArgs& a, int grid, hipStream_t st) {
     auto kern = attn_fwd_kernel<HD, NW, KS, CAUSAL, VARLEN, ROUTED, KV8, FP8>;
-    constexpr int lds = Lds<HD>::STAGE * n_stages(NW, KS, ROUTED) * KS;
+    constexpr int stage = use_dma(HD, NW, KS, ROUTED, KV8) ? LdsDma<HD>::STAGE : Lds<HD>::STAGE;
+    constexpr int lds = stage * n_stages(NW, KS, ROUTED) * KS;
     hipError_t e = set_lds(kern, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * KS * 64), lds, st, a);
