@@ -257,13 +257,23 @@ struct RouteCursor {
     int end;      // one past the last tile of the range
     int wi;       // index of the cached word, -1 for none
     uint32_t w;   // the cached word
+    uint32_t rcp; // floor((2^32 - 1) / tpb), for the group index of a tile
 
     __device__ __forceinline__ RouteCursor(const uint32_t* r, int tiles_per_bit, int e)
-        : row(r), tpb(tiles_per_bit), end(e), wi(-1), w(0) {}
+        : row(r), tpb(tiles_per_bit), end(e), wi(-1), w(0),
+          rcp(__builtin_amdgcn_readfirstlane(0xffffffffu / (uint32_t)tiles_per_bit)) {}
+
+    // t / tpb for 0 <= t < 2^31 without a division: the high product
+    // underestimates the quotient by at most one, and one step corrects it
+    __device__ __forceinline__ int group_of(int t) const {
+        uint32_t q = __umulhi((uint32_t)t, rcp);
+        if ((q + 1) * (uint32_t)tpb <= (uint32_t)t) ++q;
+        return (int)q;
+    }
 
     __device__ __forceinline__ int next(int t, bool c) {
         while (t < end) {
-            const int gi = __builtin_amdgcn_readfirstlane(t / tpb);
+            const int gi = __builtin_amdgcn_readfirstlane(group_of(t));
             if ((gi >> 5) != wi) {
                 wi = gi >> 5;
                 w = __builtin_amdgcn_readfirstlane(row[wi]);
