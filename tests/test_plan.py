@@ -160,3 +160,22 @@ def test_plan_rejects_bad_sizes_and_flags(A):
     out = (ctypes.c_int64 * 10)()
     assert lib.attn_debug_plan(1, 64, 64, 64, 4, 4, 0, 4, 16, out) != 0                     # unknown flag bit
     assert lib.attn_debug_plan(1, 64, 64, 64, 4, 4, 0, 4, 0, None) != 0                     # null output
+
+
+def test_route_group_index_rule():
+    """The route cursor finds a tile's routing group without a division:
+    q = high 32 bits of t * floor((2^32 - 1) / d), plus one if (q + 1) * d <= t.
+    The rule must equal t // d for every tile index 0 <= t < 2^31 and every
+    tiles-per-bit d >= 1 (uint32 arithmetic, no overflow in (q + 1) * d)."""
+    import random
+    rng = random.Random(7)
+    for d in list(range(1, 260)) + [1000, 4096, 65535, 65536, 1 << 20, (1 << 31) - 1]:
+        rcp = 0xFFFFFFFF // d
+        ts = list(range(0, 3000)) + [rng.randrange(0, 1 << 31) for _ in range(3000)] + \
+            [(1 << 31) - 1, (1 << 31) - 2, d - 1, d, d + 1, 32 * d - 1, 32 * d]
+        for t in ts:
+            q = (t * rcp) >> 32
+            assert (q + 1) * d < (1 << 32)
+            if (q + 1) * d <= t:
+                q += 1
+            assert q == t // d, (t, d)
