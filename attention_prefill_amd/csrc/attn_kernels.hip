@@ -102,7 +102,7 @@ __host__ __device__ constexpr int n_stages(int nw, int ks, bool routed) {
 }
 // Kernel shapes whose tiles travel from global memory to LDS directly.
 __host__ __device__ constexpr bool use_dma(int hd, int nw, int ks, bool routed, bool kv8) {
-    return ATTN_DMA && !ATTN_FUSED_KQUANT && BN == 64 && hd == 128 && !kv8 && n_stages(nw, ks, routed) == 4;
+    return ATTN_DMA && !ATTN_FUSED_KQUANT && BN == 64 && hd == 128 && !kv8 && nw >= 4;
 }
 
 // Directly loaded stages are unpadded and row-major, with the 16-byte
@@ -162,7 +162,7 @@ void attn_fwd_kernel(FwdArgs a) {
     constexpr int NST = n_stages(NW, KS, ROUTED);
     // tiles loaded straight into LDS (layout: LdsDma)
     constexpr bool DMA = use_dma(HD, NW, KS, ROUTED, KV8);
-    static_assert(!DMA || (NW == 8 && KS == 1 && HD == 128 && BN == 64 && NST == 4), "direct-load shape");
+    static_assert(!DMA || (NW >= 4 && HD == 128 && BN == 64), "direct-load shape");
     constexpr int STG = DMA ? LdsDma<HD>::STAGE : L::STAGE;     // bytes of one stage
     constexpr int KRG = DMA ? LdsDma<HD>::KREG : L::KREG;       // V tile offset in a stage
     constexpr int VBY = DMA ? LdsDma<HD>::VBYTES : L::VBYTES;   // scales follow the V tile
@@ -517,21 +517,25 @@ void attn_fwd_kernel(FwdArgs a) {
             *(f32x4*)(scl + BN + 4 * (tid - BN / 4)) = __builtin_bit_cast(f32x4, sg.svreg) * vfac;
     };
 
-    // Direct tile loads (DMA kernels): each wavefront writes whole 1 KB LDS
-    // blocks, 64 lanes x 16 bytes in lane order; each lane fetches the global
-    // chunk that the swizzled layout puts at its slot.  fp16 K and V: 16
-    // blocks of 4 rows each, two per wavefront; INT8/FP8 codes: 8 blocks of 8
-    // rows, one per wavefront, and the 64 key scales (4 bytes a lane) by
-    // wavefront 0.  Reads past the sequence end return zeros, as above.
+    // Direct tile loads (DMA kernels): each wavefront of the key group writes
+    // whole 1 KB LDS blocks, 64 lanes x 16 bytes in lane order; each lane
+    // fetches the global chunk that the swizzled layout puts at its slot.
+    // fp16 K and V: 16 blocks of 4 rows each; INT8/FP8 codes: 8 blocks of 8
+    // rows; block b goes to wavefront b % NW.  The 64 key scales (4 bytes a
+    // lane) come with wavefront 0.  Reads past the sequence end return zeros, as above.
     auto dma = [&](int kt, int stage, bool i8) __attribute__((always_inline)) {
         if constexpr (DMA) {
-            char* base = smem + stage * STG;
+            char* base = smem + (stage * KS + kgp) * STG;
             if (ROUTED && i8) {
                 const __amdgpu_buffer_rsrc_t rs = tile_rsrc(k8b, Lk * HD, TB8, kt);
-                const int row = 8 * w + (l >> 3);
-                const int c = (l & 7) ^ ((row >> 1) & 7);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, base + w * 1024), 16, row * HD + c * 16,
-                                                         0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 8 / NW; ++i) {
+                    const int blk = w + NW * i;
+                    const int row = 8 * blk + (l >> 3);
+                    const int c = (l & 7) ^ ((row >> 1) & 7);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, base + blk * 1024), 16,
+                                                             row * HD + c * 16, 0, 0, 0);
+                }
                 if (w == 0) {
                     const __amdgpu_buffer_rsrc_t ss = tile_rsrc(skb, Lk * 4, TBS, kt);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(ss, LDS_PTR(void, base + KRG + VBY), 4, l * 4, 0, 0, 0);
@@ -539,8 +543,8 @@ void attn_fwd_kernel(FwdArgs a) {
             } else {
                 const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kb, slab, TB16, kt);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int blk = 2 * w + i;
+                for (int i = 0; i < 16 / NW; ++i) {
+                    const int blk = w + NW * i;
                     const int row = 4 * blk + (l >> 4);
                     const int c = (l & 15) ^ (row & 15);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, base + blk * 1024), 16,
@@ -549,8 +553,8 @@ void attn_fwd_kernel(FwdArgs a) {
             }
             const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vb, slab, TB16, kt);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int blk = 2 * w + i;
+            for (int i = 0; i < 16 / NW; ++i) {
+                const int blk = w + NW * i;
                 const int row = 4 * blk + (l >> 4);
                 const int c = (l & 15) ^ (4 * (row & 3));
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, base + KRG + blk * 1024), 16,
@@ -860,8 +864,9 @@ void attn_fwd_kernel(FwdArgs a) {
         uint32_t* const trace = a.trace ? a.trace + (size_t)(rrow0 + m0 / TQ) * a.trace_nkt : nullptr;
         if constexpr (DMA) {
         // Direct loads: each pass starts in stage 0 with its first tile
-        // resident and its second in flight, and loads the tile two ahead of
-        // the one it computes into the stage freed two steps before.  The
+        // resident (and, with four stages, its second in flight), and loads
+        // the tile two (one) ahead of the one it computes into the stage
+        // freed two steps (one step) before.  The
         // steps of fully visible tiles are unrolled by four so that every
         // stage offset is a constant: the compiler then sees that the loads
         // in flight write other stages than the one read and waits for them
@@ -874,9 +879,13 @@ void attn_fwd_kernel(FwdArgs a) {
             auto step = [&](auto mask_tag, int S) __attribute__((always_inline)) {
                 constexpr bool MASK = decltype(mask_tag)::value;
                 if (trace && tid == 0) atomicAdd(trace + kt, C ? 0x10000u : 1u);
-                if (kn2 < kt1) dma(kn2, (S + 2) & 3, C);
+                if constexpr (NST == 4) {
+                    if (kn2 < kt1) dma(kn2, (S + 2) & 3, C);
+                } else {
+                    if (kn < kt1) dma(kn, S ^ 1, C);
+                }
                 if (MASK ? kt < kt_end : wave_active) tile(mask_tag, S, kt, C);
-                if (S & 1) dsync();
+                if (NST == 2 || (S & 1)) dsync();
                 kt = kn;
                 kn = kn2;
                 if (kn2 < kt1) kn2 = next_of(kn2 + 1, C);
@@ -886,27 +895,27 @@ void attn_fwd_kernel(FwdArgs a) {
             while (true) {
                 if (kt >= full_end) break;
                 step(std::false_type{}, 0);
-                si = 1;
+                si = 1 & (NST - 1);
                 if (kt >= full_end) break;
-                step(std::false_type{}, 1);
-                si = 2;
+                step(std::false_type{}, 1 & (NST - 1));
+                si = 2 & (NST - 1);
                 if (kt >= full_end) break;
-                step(std::false_type{}, 2);
-                si = 3;
+                step(std::false_type{}, 2 & (NST - 1));
+                si = 3 & (NST - 1);
                 if (kt >= full_end) break;
-                step(std::false_type{}, 3);
+                step(std::false_type{}, 3 & (NST - 1));
                 si = 0;
             }
             while (kt < kt1) {
                 step(std::true_type{}, si);
-                si = (si + 1) & 3;
+                si = (si + 1) & (NST - 1);
             }
             dsync();
         };
         int kt = next_of(kt0, false);
         int kt2 = kt < kt1 ? next_of(kt + 1, false) : kt1;
         if (kt < kt1) dma(kt, 0, false);
-        if (kt2 < kt1) dma(kt2, 1, false);
+        if (NST == 4 && kt2 < kt1) dma(kt2, 1, false);
         query_prologue();
         dsync();
         dpass(std::false_type{}, kt);
@@ -914,7 +923,7 @@ void attn_fwd_kernel(FwdArgs a) {
         kt2 = kt < kt1 ? next_of(kt + 1, true) : kt1;
         if (kt < kt1) {
             dma(kt, 0, true);
-            if (kt2 < kt1) dma(kt2, 1, true);
+            if (NST == 4 && kt2 < kt1) dma(kt2, 1, true);
             float sq;
             quantize_q_regs<HD, FP8>(qf, q8, sq);
             sq_mul = sq > 0.0f ? sq : 1.0f;
@@ -1000,34 +1009,41 @@ void attn_fwd_kernel(FwdArgs a) {
         }
         }
     } else if constexpr (DMA) {
-    // Direct loads (one key group): tiles 0 and 1 in stages 0 and 1; step it
-    // loads tile it + 2 into the stage step it - 2 read, computes tile it
-    // and, after odd steps, waits for its loads and meets the barrier.  Fully
+    // Direct loads, four stages (one key group): tiles 0 and 1 in stages 0
+    // and 1; step it loads tile it + 2 into the stage step it - 2 read,
+    // computes tile it and, after odd steps, waits for its loads and meets
+    // the barrier.  Two stages (per key group): step it loads tile it + 1 into
+    // the stage step it - 1 read and every step ends with the wait and the
+    // barrier.  Fully
     // visible tiles run unrolled by four with constant stage offsets (see the
     // routed passes), the masked tail with a computed stage.
     if (has(0)) dma(kt_first, 0, false);
-    if (has(1)) dma(kt_first + 1, 1, false);
+    if (NST == 4 && has(1)) dma(kt_first + KS, 1, false);
     query_prologue();
     dsync();
     auto dstep = [&](auto mask_tag, int S, int it) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const int kt = kt_first + it;
-        if (has(it + 2)) dma(kt + 2, (S + 2) & 3, false);
+        const int kt = kt_first + KS * it;
+        if constexpr (NST == 4) {
+            if (has(it + 2)) dma(kt + 2 * KS, (S + 2) & 3, false);
+        } else {
+            if (has(it + 1)) dma(kt + KS, S ^ 1, false);
+        }
         if (MASK ? kt < kt_end : wave_active) tile(mask_tag, S, kt, false);
-        if (S & 1) dsync();
+        if (NST == 2 || (S & 1)) dsync();
     };
     int it = 0;
     while (true) {
         if (it >= it_full) break;
         dstep(std::false_type{}, 0, it++);
         if (it >= it_full) break;
-        dstep(std::false_type{}, 1, it++);
+        dstep(std::false_type{}, 1 & (NST - 1), it++);
         if (it >= it_full) break;
-        dstep(std::false_type{}, 2, it++);
+        dstep(std::false_type{}, 2 & (NST - 1), it++);
         if (it >= it_full) break;
-        dstep(std::false_type{}, 3, it++);
+        dstep(std::false_type{}, 3 & (NST - 1), it++);
     }
-    for (; it < n_it; ++it) dstep(std::true_type{}, it & 3, it);
+    for (; it < n_it; ++it) dstep(std::true_type{}, it & (NST - 1), it);
     } else {
     // Prologue: the first PF tiles' loads go out behind the query loads, and
     // one wait covers them all.
@@ -1106,7 +1122,7 @@ void attn_fwd_kernel(FwdArgs a) {
         // groups, so the merge is lane by lane: O = sum_g 2^(m_g - m) O_g,
         // l likewise, m = max_g m_g.
         constexpr int NE4 = NDB * 4 + 1;       // f32x4 slots per lane: O, then (m, l)
-        static_assert((KS - 1) * NW * NE4 * 64 * 16 <= L::TOTAL * KS, "merge buffer exceeds LDS");
+        static_assert((KS - 1) * NW * NE4 * 64 * 16 <= STG * NST * KS, "merge buffer exceeds LDS");
         f32x4* xb = (f32x4*)smem;
         if (kgp > 0) {
             f32x4* dst = xb + (size_t)((kgp - 1) * NW + w) * NE4 * 64 + l;
