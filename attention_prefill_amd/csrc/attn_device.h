@@ -203,27 +203,28 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 }
 
 // Four 8-key operand fragments from transposed reads: fragment i takes the
-// two reads at LDS byte address a_i and a_i + 1024 (its keys 0-3 and 4-7 of
-// a row-major [key][d] tile with 256-byte rows).  The reads and the wait for
+// two reads at LDS byte address a_i and a_i + H (its keys 0-3 and 4-7 of a
+// row-major [key][d] tile whose rows are H / 4 bytes).  The reads and the wait for
 // them are one asm block: written with the builtin, every such read would be
 // made to wait for all direct tile loads in flight, which the compiler
 // cannot tell apart from it; the barrier protocol of the callers already
 // orders these reads after the loads of their stage.
+template <int H>
 __device__ __forceinline__ void lds_read_tr16_x4(unsigned a0, unsigned a1, unsigned a2, unsigned a3,
                                                  f16x8 (&f)[4]) {
     f16x4 r0, r1, r2, r3, r4, r5, r6, r7;
     asm volatile(
         "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
         "ds_read_b64_tr_b16 %2, %9\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
         "ds_read_b64_tr_b16 %4, %10\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
         "ds_read_b64_tr_b16 %6, %11\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "i"(H)
         : "memory");
     f[0] = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
     f[1] = __builtin_shufflevector(r2, r3, 0, 1, 2, 3, 4, 5, 6, 7);

@@ -102,18 +102,20 @@ __host__ __device__ constexpr int n_stages(int nw, int ks, bool routed) {
 }
 // Kernel shapes whose tiles travel from global memory to LDS directly.
 __host__ __device__ constexpr bool use_dma(int hd, int nw, int ks, bool routed, bool kv8) {
-    return ATTN_DMA && !ATTN_FUSED_KQUANT && BN == 64 && hd == 128 && !kv8 && nw >= 4;
+    return ATTN_DMA && !ATTN_FUSED_KQUANT && BN == 64 && (hd == 128 || hd == 64) && !kv8 && nw >= 2;
 }
 
 // Directly loaded stages are unpadded and row-major, with the 16-byte
 // chunks of each row permuted by an XOR of the row index, so that the
 // operand reads of 16 lanes (16-byte reads) or 32 lanes (8-byte transposed
 // reads), all at one column of different rows, fall on distinct banks:
-// - fp16 K, 16 chunks per row: chunk c of row r at c ^ (r & 15);
-// - INT8 / FP8 K codes, 8 chunks per 128-byte row (two rows per bank
-//   sweep): chunk c of row r at c ^ ((r >> 1) & 7);
-// - V, [key][d], 16 chunks per row, read four keys by 4 x 4 d at a time:
-//   chunk c of key r at c ^ (4 * (r & 3)).
+// - fp16 K: chunk c of row r at c ^ (r & 15) (hdim 128, 16 chunks per
+//   256-byte row) or c ^ ((r >> 1) & 7) (hdim 64, 8 chunks per 128-byte
+//   row, two rows per bank sweep);
+// - INT8 / FP8 K codes: c ^ ((r >> 1) & 7) (hdim 128, 128-byte rows) or
+//   c ^ ((r >> 2) & 3) (hdim 64, 64-byte rows);
+// - V, [key][d], read four keys by 4 x 4 d at a time: chunk c of key r at
+//   c ^ (4 * (r & 3)) (hdim 128) or c ^ (4 * ((r >> 1) & 1)) (hdim 64).
 // The per-key scales of a tile follow the V tile (raw s_k, then s_v).
 template <int HD>
 struct LdsDma {
@@ -123,6 +125,17 @@ struct LdsDma {
     static constexpr int SCL = 2 * BN * 4;
     static constexpr int STAGE = KREG + VBYTES + SCL;
     static constexpr int TOTAL = 2 * STAGE;
+    static constexpr int CPR = HD * 2 / 16;       // 16-byte chunks per fp16 row
+    static constexpr int KRPB = 1024 / (HD * 2);  // fp16 rows per 1 KB load block
+    static constexpr int KBLK = BN / KRPB;        // load blocks per fp16 tile
+    static constexpr int C8PR = HD / 16;          // 16-byte chunks per code row
+    static constexpr int K8RPB = 1024 / HD;       // code rows per load block
+    static constexpr int K8BLK = BN / K8RPB;      // load blocks per code tile
+    // chunk permutations: rows that share a 256-byte bank sweep (1, 2 or 4
+    // of them) keep their natural order and the next rows are XORed apart
+    __device__ static int kswz(int r) { return (r / (256 / (HD * 2))) & (CPR - 1); }
+    __device__ static int k8swz(int r) { return (r / (256 / HD)) & (C8PR - 1); }
+    __device__ static int vswz(int r) { return HD == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 template <int HD>
@@ -155,14 +168,16 @@ void attn_fwd_kernel(FwdArgs a) {
     constexpr int VBLK = (BN / 4) * (HD / 8);          // 4-key x 8-d V blocks per tile
     constexpr int VB = (VBLK + NT - 1) / NT;           // V blocks per thread
     constexpr int NDB = HD / 32;                       // 32-row blocks of d in O^T
-    // Tiles in flight ahead of the one computed.  Two need a second staging
-    // set, which only the hdim-64 FP16 kernel has registers for.
-    constexpr int PF = (HD == 64 && !ROUTED && !KV8 && NW == 4 && BN == 64) ? 2 : 1;
     // four LDS stages and tiles stored two ahead: a barrier every other tile
     constexpr int NST = n_stages(NW, KS, ROUTED);
     // tiles loaded straight into LDS (layout: LdsDma)
     constexpr bool DMA = use_dma(HD, NW, KS, ROUTED, KV8);
-    static_assert(!DMA || (NW >= 4 && HD == 128 && BN == 64), "direct-load shape");
+    static_assert(!DMA || (NW >= 2 && (HD == 128 || HD == 64) && BN == 64), "direct-load shape");
+    // Tiles in flight ahead of the one computed, on the register path.  Two
+    // need a second staging set, which only the hdim-64 FP16 kernel has
+    // registers for.
+    constexpr int PF = (HD == 64 && !ROUTED && !KV8 && NW == 4 && BN == 64 && !DMA) ? 2 : 1;
+    using DG = LdsDma<HD>;
     constexpr int STG = DMA ? LdsDma<HD>::STAGE : L::STAGE;     // bytes of one stage
     constexpr int KRG = DMA ? LdsDma<HD>::KREG : L::KREG;       // V tile offset in a stage
     constexpr int VBY = DMA ? LdsDma<HD>::VBYTES : L::VBYTES;   // scales follow the V tile
@@ -529,12 +544,13 @@ void attn_fwd_kernel(FwdArgs a) {
             if (ROUTED && i8) {
                 const __amdgpu_buffer_rsrc_t rs = tile_rsrc(k8b, Lk * HD, TB8, kt);
 #pragma unroll
-                for (int i = 0; i < 8 / NW; ++i) {
+                for (int i = 0; i < (DG::K8BLK + NW - 1) / NW; ++i) {
                     const int blk = w + NW * i;
-                    const int row = 8 * blk + (l >> 3);
-                    const int c = (l & 7) ^ ((row >> 1) & 7);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, base + blk * 1024), 16,
-                                                             row * HD + c * 16, 0, 0, 0);
+                    const int row = DG::K8RPB * blk + l / DG::C8PR;
+                    const int c = (l % DG::C8PR) ^ DG::k8swz(row);
+                    if (DG::K8BLK % NW == 0 || blk < DG::K8BLK)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, base + blk * 1024), 16,
+                                                                 row * HD + c * 16, 0, 0, 0);
                 }
                 if (w == 0) {
                     const __amdgpu_buffer_rsrc_t ss = tile_rsrc(skb, Lk * 4, TBS, kt);
@@ -543,22 +559,24 @@ void attn_fwd_kernel(FwdArgs a) {
             } else {
                 const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kb, slab, TB16, kt);
 #pragma unroll
-                for (int i = 0; i < 16 / NW; ++i) {
+                for (int i = 0; i < (DG::KBLK + NW - 1) / NW; ++i) {
                     const int blk = w + NW * i;
-                    const int row = 4 * blk + (l >> 4);
-                    const int c = (l & 15) ^ (row & 15);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, base + blk * 1024), 16,
-                                                             row * (HD * 2) + c * 16, 0, 0, 0);
+                    const int row = DG::KRPB * blk + l / DG::CPR;
+                    const int c = (l % DG::CPR) ^ DG::kswz(row);
+                    if (DG::KBLK % NW == 0 || blk < DG::KBLK)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(void, base + blk * 1024), 16,
+                                                                 row * (HD * 2) + c * 16, 0, 0, 0);
                 }
             }
             const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vb, slab, TB16, kt);
 #pragma unroll
-            for (int i = 0; i < 16 / NW; ++i) {
+            for (int i = 0; i < (DG::KBLK + NW - 1) / NW; ++i) {
                 const int blk = w + NW * i;
-                const int row = 4 * blk + (l >> 4);
-                const int c = (l & 15) ^ (4 * (row & 3));
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, base + KRG + blk * 1024), 16,
-                                                         row * (HD * 2) + c * 16, 0, 0, 0);
+                const int row = DG::KRPB * blk + l / DG::CPR;
+                const int c = (l % DG::CPR) ^ DG::vswz(row);
+                if (DG::KBLK % NW == 0 || blk < DG::KBLK)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, base + KRG + blk * 1024), 16,
+                                                             row * (HD * 2) + c * 16, 0, 0, 0);
             }
         }
     };
@@ -587,16 +605,18 @@ void attn_fwd_kernel(FwdArgs a) {
     // and the 4 consecutive keys of each read.
     int koff[DMA ? HD / 16 : 1], k8off[DMA ? HD / 32 : 1], voff[DMA ? NDB : 1];
     if constexpr (DMA) {
+        // rows 32*kb32 + krow share the swizzle of krow (32 is a multiple of
+        // every swizzle period)
 #pragma unroll
         for (int t = 0; t < HD / 16; ++t)
-            koff[t] = krow * (HD * 2) + (((2 * g + 4 * (t / 2) + (t % 2)) ^ (krow & 15)) << 4);
+            koff[t] = krow * (HD * 2) + (((2 * g + 4 * (t / 2) + (t % 2)) ^ DG::kswz(krow)) << 4);
 #pragma unroll
-        for (int j = 0; j < HD / 32; ++j) k8off[j] = krow * HD + (((g + 2 * j) ^ ((krow >> 1) & 7)) << 4);
+        for (int j = 0; j < HD / 32; ++j) k8off[j] = krow * HD + (((g + 2 * j) ^ DG::k8swz(krow)) << 4);
         const int q4 = (l >> 2) & 3;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             voff[db] = (8 * (l >> 5) + q4) * (HD * 2) +
-                       ((4 * (db ^ q4) + 2 * ((l >> 4) & 1) + ((l & 3) >> 1)) << 4) + 8 * (l & 1);
+                       (((4 * db + 2 * ((l >> 4) & 1) + ((l & 3) >> 1)) ^ DG::vswz(q4)) << 4) + 8 * (l & 1);
     }
 
     // One key tile: scores, optional mask, online softmax, P.V.
@@ -678,14 +698,33 @@ void attn_fwd_kernel(FwdArgs a) {
                 for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
                     for (int t = 0; t < HD / 16; ++t)
-                        kfr[kb32][t] = *(const f16x8*)(k16 + (32 * kb32 + krow) * L::KP + 16 * g +
-                                                       32 * (t / 2) + 8 * (t % 2));
-                const _Float16* vrow = vt + lq * L::VTP + 8 * g;
+                        kfr[kb32][t] = DMA ? *(const f16x8*)(kbuf + 32 * kb32 * (HD * 2) + koff[DMA ? t : 0])
+                                           : *(const f16x8*)(k16 + (32 * kb32 + krow) * L::KP + 16 * g +
+                                                             32 * (t / 2) + 8 * (t % 2));
+                if constexpr (DMA) {
+                    static_assert(NDB == 2, "up-front transposed reads: two d blocks");
+                    // two 16-key steps per asm block: fragments (kk, 0), (kk, 1),
+                    // (kk + 1, 0), (kk + 1, 1)
 #pragma unroll
-                for (int kk = 0; kk < 2 * NKB; ++kk)
+                    for (int kk = 0; kk < 2 * NKB; kk += 2) {
+                        const unsigned va = lds_addr(vt) + kk * 16 * (HD * 2);
+                        const unsigned vb2 = va + 16 * (HD * 2);
+                        f16x8 fr[4];
+                        lds_read_tr16_x4<4 * (HD * 2)>(va + voff[0], va + voff[DMA ? 1 : 0], vb2 + voff[0],
+                                                       vb2 + voff[DMA ? 1 : 0], fr);
+                        vfr[kk][0] = fr[0];
+                        vfr[kk][DMA ? 1 : 0] = fr[1];
+                        vfr[kk + 1][0] = fr[2];
+                        vfr[kk + 1][DMA ? 1 : 0] = fr[3];
+                    }
+                } else {
+                    const _Float16* vrow = vt + lq * L::VTP + 8 * g;
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        vfr[kk][db] = *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
+                    for (int kk = 0; kk < 2 * NKB; ++kk)
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+                            vfr[kk][db] = *(const f16x8*)(vrow + (32 * db) * L::VTP + 16 * kk);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kb32 = 0; kb32 < NKB; ++kb32) {
@@ -735,6 +774,28 @@ void attn_fwd_kernel(FwdArgs a) {
         // O^T += V^T P^T over the two 16-key steps of one 32-key block
         const _Float16* vrow = vt + lq * L::VTP + 8 * g;
         auto pv = [&](int kb32, const f16x8(&pkb)[2]) __attribute__((always_inline)) {
+            if constexpr (DMA && NDB == 2) {
+                // keys 16kk + 8(l/32) + 0..7 of d = 32db + l%32 for both 16-key
+                // steps of the block (already read when up front)
+                f16x8 fr[4];
+                if (EARLY && !(ROUTED && i8)) {
+                    fr[0] = vfr[2 * kb32][0];
+                    fr[1] = vfr[2 * kb32][EARLY ? 1 : 0];
+                    fr[2] = vfr[EARLY ? 2 * kb32 + 1 : 0][0];
+                    fr[3] = vfr[EARLY ? 2 * kb32 + 1 : 0][EARLY ? 1 : 0];
+                } else {
+                    const unsigned va = lds_addr(vt) + 2 * kb32 * 16 * (HD * 2);
+                    const unsigned vb2 = va + 16 * (HD * 2);
+                    lds_read_tr16_x4<4 * (HD * 2)>(va + voff[0], va + voff[DMA ? 1 : 0], vb2 + voff[0],
+                                                   vb2 + voff[DMA ? 1 : 0], fr);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int db = 0; db < 2; ++db)
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[2 * t + db], pkb[t], o[db], 0, 0, 0);
+                return;
+            }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int kk = 2 * kb32 + t;
@@ -742,8 +803,9 @@ void attn_fwd_kernel(FwdArgs a) {
                     // keys 16kk + 8(l/32) + 0..7 of d = 32db + l%32, every db
                     const unsigned va = lds_addr(vt) + kk * 16 * (HD * 2);
                     f16x8 fr[4];
-                    lds_read_tr16_x4(va + voff[0], va + voff[DMA ? 1 : 0], va + voff[DMA ? 2 : 0],
-                                     va + voff[DMA ? 3 : 0], fr);
+                    lds_read_tr16_x4<4 * (HD * 2)>(va + voff[0], va + voff[DMA && NDB == 4 ? 1 : 0],
+                                                   va + voff[DMA && NDB == 4 ? 2 : 0],
+                                                   va + voff[DMA && NDB == 4 ? 3 : 0], fr);
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
                         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[db], pkb[t], o[db], 0, 0, 0);
