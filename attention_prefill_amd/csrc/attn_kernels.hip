@@ -18,22 +18,27 @@
 //     Grid order is heavy-first for causal
 //     masks and keeps the workgroups of one kv head on one XCD (index mod 8)
 //     when the number of head groups is a multiple of 8.
-//   * tile loader: 64-key K and V tiles go global -> registers -> LDS
-//     through buffer descriptors (reads past the sequence end return zeros),
-//     with two LDS stages and one barrier per tile.  The hdim-64 FP16 kernel
-//     keeps two register sets so that the loads of tile t+2 are in flight
-//     while tile t is computed; the others load tile t+1.
+//   * tile loader: 64-key K and V tiles (and INT8/FP8 codes with their
+//     scales) are read through buffer descriptors that end at the sequence's
+//     last byte (reads past it return zeros).  The fp16 and routed kernels
+//     load them straight into LDS (buffer loads with LDS as the
+//     destination) in an XOR-swizzled row-major layout, four stages with
+//     the tile two ahead and a barrier every other tile for eight
+//     wavefronts, two stages and a barrier per tile otherwise.  The INT8
+//     key/value-cache kernels go global -> registers -> LDS, widening the
+//     codes to fp16 on the way.
 //   * score MFMA: the transposed score tile S^T = K Q^T is computed with
-//     v_mfma_f32_32x32x16_f16 (FP16 route) or v_mfma_i32_32x32x32_i8 (INT8
-//     route).  In the 32x32 accumulator layout a lane then owns one query
+//     v_mfma_f32_32x32x16_f16 (FP16 route), v_mfma_i32_32x32x32_i8 (INT8
+//     route) or v_mfma_f32_32x32x64_f8f6f4 on e4m3 codes (FP8 route).  In the 32x32 accumulator layout a lane then owns one query
 //     (column) and 16 keys, so row max / row sum are in-register plus one
 //     v_permlane32_swap between the two half-waves.  K rows are read with
 //     bits 2 and 3 of the row index swapped; this makes the score layout
 //     coincide with the B-operand layout of the P.V MFMA, so P never leaves
 //     registers.
-//   * P.V MFMA: O^T += V^T P^T with v_mfma_f32_32x32x16_f16.  V is stored
-//     transposed in LDS ([d][key], transposed in registers by the loader),
-//     so each V^T fragment (8 keys of one d) is one 16-byte read.
+//   * P.V MFMA: O^T += V^T P^T with v_mfma_f32_32x32x16_f16.  Directly
+//     loaded V stays [key][d] in LDS and each V^T fragment (8 keys of one d)
+//     is two transposed 8-byte reads (ds_read_b64_tr_b16); the register
+//     path stores V transposed, [d][key], for one 16-byte read.
 //   * online softmax in base 2 with the scale folded into one FMA per
 //     score; O is rescaled only when some row max of the wavefront moved by
 //     more than a threshold.
@@ -87,12 +92,13 @@ constexpr int NKB = BN / 32;        // 32-key score blocks per tile
 #define ATTN_DMA 1
 #endif
 // ---------------------------------------------------------------------------
-// LDS layout of one stage: the K tile (fp16 [key][d], or INT8 codes
-// [key][d]), the V tile stored transposed, [d][key], so that the P.V operand
-// (8 consecutive keys of one d) is a single 16-byte read, and the tile's
-// per-key scales (K scales times |scale|*log2(e), then V scales; INT8 tiles
-// and INT8 key/value caches).  Row pitches are padded so that the
-// row-parallel operand reads and the staging writes spread over the banks.
+// LDS layout of one stage on the register path (INT8 key/value caches; the
+// directly loaded layout is LdsDma below): the K tile (fp16 [key][d], or
+// INT8 codes [key][d]), the V tile stored transposed, [d][key], so that the
+// P.V operand (8 consecutive keys of one d) is a single 16-byte read, and
+// the tile's per-key scales (K scales times |scale|*log2(e), then V scales).
+// Row pitches are padded so that the row-parallel operand reads and the
+// staging writes spread over the banks.
 // ---------------------------------------------------------------------------
 // LDS stages of a kernel shape: the eight-wavefront kernels keep four
 // (tiles are stored two ahead, so one barrier covers two tiles); the others
@@ -283,6 +289,7 @@ void attn_fwd_kernel(FwdArgs a) {
     float vfac = 1.0f, vfac_inv = 1.0f;
 
     // ---- tile loader ------------------------------------------------------------
+    // Register path (gload / lstore; the direct loads are `dma` below).
     // K: 16-byte chunks of rows.  V: per thread a block of 4 keys x 8 d, read as
     // four 16-byte row pieces and written transposed as eight 8-byte pieces.
     // Loads go through buffer resources covering one tile and the rest of this
@@ -872,7 +879,8 @@ void attn_fwd_kernel(FwdArgs a) {
 
     // Iteration it covers tiles kt0 + KS*it .. + KS-1, one per key group; the
     // first it_full iterations have every tile below nfull.  Tile it of this
-    // group lives in staging set it % PF and LDS stage it % 2.
+    // group lives in LDS stage it % NST (and, on the register path, in
+    // staging set it % PF).
     const int n_it = (kt1 - kt0 + KS - 1) / KS;
     const int it_full = max(0, (min(nfull, kt1) - kt0) / KS);
     const int kt_first = kt0 + kgp;
