@@ -248,8 +248,10 @@ __device__ __forceinline__ u32x2 widen_i8x4(unsigned w) {
 // [t, end) of one route: next(t, c) is the first tile >= t whose group's bit
 // is c, or end.  It scans the cached word with a count of trailing zeros
 // (of ~word for route 0) and reads a new word every 32 groups; a start
-// inside a group or a word is allowed.  Every value is uniform over the
-// wavefront.  The forward kernel's routed passes and the route-dump test
+// inside a group or a word is allowed.  Each decode also records the run of
+// consecutive groups of that route (within the cached word) around the tile
+// it returns, so that the calls that follow inside the run, one per tile,
+// return at once.  Every value is uniform over the wavefront.  The forward kernel's routed passes and the route-dump test
 // hook both walk their tiles with this cursor.
 // ---------------------------------------------------------------------------
 struct RouteCursor {
@@ -259,10 +261,14 @@ struct RouteCursor {
     int wi;       // index of the cached word, -1 for none
     uint32_t w;   // the cached word
     uint32_t rcp; // floor((2^32 - 1) / tpb), for the group index of a tile
+    int run_lo;   // tiles [run_lo, run_hi) are known to take route run_c
+    int run_hi;
+    bool run_c;
 
     __device__ __forceinline__ RouteCursor(const uint32_t* r, int tiles_per_bit, int e)
         : row(r), tpb(tiles_per_bit), end(e), wi(-1), w(0),
-          rcp(__builtin_amdgcn_readfirstlane(0xffffffffu / (uint32_t)tiles_per_bit)) {}
+          rcp(__builtin_amdgcn_readfirstlane(0xffffffffu / (uint32_t)tiles_per_bit)),
+          run_lo(0), run_hi(0), run_c(false) {}
 
     // t / tpb for 0 <= t < 2^31 without a division: the high product
     // underestimates the quotient by at most one, and one step corrects it
@@ -273,6 +279,7 @@ struct RouteCursor {
     }
 
     __device__ __forceinline__ int next(int t, bool c) {
+        if (c == run_c && t >= run_lo && t < run_hi) return t;
         while (t < end) {
             const int gi = __builtin_amdgcn_readfirstlane(group_of(t));
             if ((gi >> 5) != wi) {
@@ -280,7 +287,20 @@ struct RouteCursor {
                 w = __builtin_amdgcn_readfirstlane(row[wi]);
             }
             const uint32_t wv = (c ? w : ~w) >> (gi & 31);
-            if (wv) return min(end, max(t, (gi + (int)__builtin_ctz(wv)) * tpb));
+            if (wv) {
+                // first group of route c at or after gi, and the length of
+                // the run of route-c groups it starts (to the word's end at
+                // most: the bits shifted in above it are zeros)
+                const int k0 = (int)__builtin_ctz(wv);
+                const uint32_t rest = ~(wv >> k0);
+                const int n1 = rest ? (int)__builtin_ctz(rest) : 32;
+                const int gf = gi + k0;
+                const int r = min(end, max(t, gf * tpb));
+                run_c = c;
+                run_lo = r;
+                run_hi = min(end, (gf + n1) * tpb);
+                return r;
+            }
             t = (wi + 1) * 32 * tpb;
         }
         return end;
