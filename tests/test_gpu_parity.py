@@ -222,6 +222,29 @@ def test_gpu_routed_split_keys(A, orc, monkeypatch, d, tpb, causal, lowp, ks, wa
     check(got.cpu().numpy(), ref, (lowp, ks))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("ks", ["2", "3", "8"])
+def test_gpu_split_merge_repeatable(A, orc, monkeypatch, d, ks):
+    """Key splits and their merge (summed in split order) give bit-identical
+    outputs on repeated calls, with another split call of a different grid
+    between them, dense and packed, and agree with the oracle."""
+    rng = np.random.default_rng(4700 + d + int(ks))
+    monkeypatch.setenv("ATTN_KSPLIT", ks)
+    q, k, v = rand16(rng, (2, 4, 150, d)), rand16(rng, (2, 2, 1500, d)), rand16(rng, (2, 2, 1500, d))
+    cu = [0, 700, 1150, 1900]
+    pq, pk, pv = rand16(rng, (4, 1900, d)), rand16(rng, (2, 1900, d)), rand16(rng, (2, 1900, d))
+    say("split merge repeat d=%d splits=%s" % (d, ks))
+    dense = [gpu_attn(A, q, k, v, 0.09, True) for _ in range(2)]
+    packed = gpu_attn(A, pq, pk, pv, 0.09, True, cu=cu)
+    dense.append(gpu_attn(A, q, k, v, 0.09, True))
+    packed2 = gpu_attn(A, pq, pk, pv, 0.09, True, cu=cu)
+    for o in dense[1:]:
+        assert np.array_equal(o.view(np.uint16), dense[0].view(np.uint16))
+    assert np.array_equal(packed.view(np.uint16), packed2.view(np.uint16))
+    check(dense[0], orc.attn_fwd(q, k, v, scale=0.09, causal=True), ("dense", ks))
+    check(packed, orc.attn_fwd(pq, pk, pv, scale=0.09, causal=True, cu_seqlens=cu), ("packed", ks))
+
+
 @pytest.mark.parametrize("waves", ["4", "8"])
 def test_gpu_routed_varlen_zero_mask_is_dense(A, monkeypatch, waves):
     """Routed calls run one key group; both calls are pinned to the same
