@@ -283,9 +283,10 @@ void attn_fwd_kernel(FwdArgs a) {
 
     i32x4 q8[ROUTED ? HD / 32 : 1];     // INT8 query codes (routed), set after the prologue wait
     float sq_mul = 1.0f;
-    // INT8 value cache: the value scales enter P relative to a power of two
-    // (vfac = 2^-e, with 2^e near the largest scale of the workgroup's key
-    // range), which the epilogue multiplies back (vfac_inv, exact)
+    // INT8 value cache: the value scales enter the staged V relative to a
+    // power of two (vfac = 2^-e, with 2^e near the largest scale of the
+    // workgroup's key range), which the epilogue multiplies back (vfac_inv,
+    // exact)
     float vfac = 1.0f, vfac_inv = 1.0f;
 
     // ---- tile loader ------------------------------------------------------------
@@ -308,8 +309,8 @@ void attn_fwd_kernel(FwdArgs a) {
         u32x4 kreg[KCH];
         u32x4 vreg[VB][4];
         u32x2 v8reg[VB][4];     // INT8 V cache: 8 codes of each of 4 keys
+        u32x4 svk[VB];          // ... and the scales of those 4 keys
         u32x4 skreg;
-        u32x4 svreg;
     };
     // The two-set pipeline waits for the older set with a load count, so every
     // lane issues the same number of loads: the first half of the waves loads
@@ -392,6 +393,7 @@ void attn_fwd_kernel(FwdArgs a) {
         }
         if constexpr (KV8) {
             const __amdgpu_buffer_rsrc_t v8rs = tile_rsrc(v8b, Lk * HD, TB8, kt);
+            const __amdgpu_buffer_rsrc_t svrs = tile_rsrc(svb, Lk * 4, TBS, kt);
 #pragma unroll
             for (int n = 0; n < VB; ++n) {
                 const int bi = tid + n * NT;
@@ -402,12 +404,8 @@ void attn_fwd_kernel(FwdArgs a) {
                     for (int i = 0; i < 4; ++i)
                         sg.v8reg[n][i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
                             v8rs, (4 * kg + i) * HD + 8 * dc, 0, 0));
+                    sg.svk[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(svrs, kg * 16, 0, 0));
                 }
-            }
-            if (tid >= BN / 4 && tid < BN / 2) {
-                const __amdgpu_buffer_rsrc_t svrs = tile_rsrc(svb, Lk * 4, TBS, kt);
-                sg.svreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    svrs, (tid - BN / 4) * 16, 0, 0));
             }
         } else {
             const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(vb, slab, TB16, kt);
@@ -512,15 +510,20 @@ void attn_fwd_kernel(FwdArgs a) {
                 const int dc = bi / (BN / 4);
                 u32x4 r0w = vreg[n][0], r1w = vreg[n][1], r2w = vreg[n][2], r3w = vreg[n][3];
                 if constexpr (KV8) {
-                    // INT8 value cache: rows of 8 codes widened to 8 fp16 values
-                    auto row8 = [](u32x2 c) __attribute__((always_inline)) {
+                    // INT8 value cache: each key's row of 8 codes widened to
+                    // fp16 (exact) and multiplied by the key's scale times
+                    // vfac, rounded to fp16 (the products stay below 2^8)
+                    const f32x4 sv4 = __builtin_bit_cast(f32x4, sg.svk[n]) * vfac;
+                    auto row8 = [](u32x2 c, float sv) __attribute__((always_inline)) {
                         const u32x2 a0 = widen_i8x4(c[0]), a1 = widen_i8x4(c[1]);
-                        return u32x4{a0[0], a0[1], a1[0], a1[1]};
+                        const f16x2 h = {(_Float16)sv, (_Float16)sv};
+                        auto mul = [&](unsigned w) { return __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, w) * h); };
+                        return u32x4{mul(a0[0]), mul(a0[1]), mul(a1[0]), mul(a1[1])};
                     };
-                    r0w = row8(sg.v8reg[n][0]);
-                    r1w = row8(sg.v8reg[n][1]);
-                    r2w = row8(sg.v8reg[n][2]);
-                    r3w = row8(sg.v8reg[n][3]);
+                    r0w = row8(sg.v8reg[n][0], sv4[0]);
+                    r1w = row8(sg.v8reg[n][1], sv4[1]);
+                    r2w = row8(sg.v8reg[n][2], sv4[2]);
+                    r3w = row8(sg.v8reg[n][3], sv4[3]);
                 }
                 _Float16* dst = vt + (8 * dc) * L::VTP + 4 * kg;
 #pragma unroll
@@ -535,8 +538,6 @@ void attn_fwd_kernel(FwdArgs a) {
                 }
             }
         }
-        if (KV8 && tid >= BN / 4 && tid < BN / 2)
-            *(f32x4*)(scl + BN + 4 * (tid - BN / 4)) = __builtin_bit_cast(f32x4, sg.svreg) * vfac;
     };
 
     // Direct tile loads (DMA kernels): each wavefront of the key group writes
@@ -636,7 +637,6 @@ void attn_fwd_kernel(FwdArgs a) {
         f16x8 vfr[EARLY ? 2 * NKB : 1][EARLY ? NDB : 1];   // V fragments requested with K
         // per-key scales of the tile (INT8 tiles, key/value caches)
         const float* skc = (const float*)(kbuf + KRG + VBY);
-        const float* svc = skc + BN;
         // x[kb32][i] *= the scale of its key: this lane's keys are
         // 32*kb32 + 8*g + (i%8) + 16*(i/8)
         auto key_scale = [&](int kb32) __attribute__((always_inline)) {
@@ -849,18 +849,11 @@ void attn_fwd_kernel(FwdArgs a) {
         for (int kb32 = 0; kb32 < NKB; ++kb32)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                // value-cache scales of keys 32*kb32 + 8*g + 16*t + j: the P that
-                // multiplies the widened V codes is p * s_v (the sum keeps p)
-                f32x4 v0 = f32x4{1.0f, 1.0f, 1.0f, 1.0f}, v1 = v0;
-                if constexpr (KV8) {
-                    v0 = *(const f32x4*)(svc + 32 * kb32 + 8 * g + 16 * t);
-                    v1 = *(const f32x4*)(svc + 32 * kb32 + 8 * g + 16 * t + 4);
-                }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[kb32][8 * t + j], amul, nm));
                     rs += p;
-                    pk[kb32][t][j] = (_Float16)(KV8 ? p * (j < 4 ? v0[j] : v1[j - 4]) : p);
+                    pk[kb32][t][j] = (_Float16)p;
                 }
             }
         l_run += rs;
@@ -889,12 +882,12 @@ void attn_fwd_kernel(FwdArgs a) {
     const int kt_end = min(w_nkt, kt1);
 
     if constexpr (KV8) {
-        // The value-cache scales multiply P before its fp16 rounding.  P
-        // reaches 2^TAU between rescales, so the scales are first brought to
-        // [1, 2) at their largest by an exact power of two: p * s_v * vfac
-        // stays below 2^(TAU+1) (no overflow for any scale), and keys whose
-        // scale is near the largest keep full fp16 precision whatever the
-        // value magnitude (no subnormal P for small values).
+        // The value-cache scales multiply the widened codes as the V tile is
+        // staged (one fp16 product per value, once per workgroup), first
+        // brought to [1, 2) at their largest by an exact power of two:
+        // code * s_v * vfac stays below 2^8 (no overflow for any scale), and
+        // keys whose scale is near the largest keep full fp16 precision
+        // whatever the value magnitude (no subnormal values).
         float mx = 0.0f;
         const int j1 = min(kt1 * BN, Lk);
         for (int j = kt0 * BN + (int)threadIdx.x; j < j1; j += NW * KS * 64) mx = fmaxf(mx, fabsf(svb[j]));
