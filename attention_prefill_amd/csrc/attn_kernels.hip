@@ -288,6 +288,9 @@ void attn_fwd_kernel(FwdArgs a) {
     // workgroup's key range), which the epilogue multiplies back (vfac_inv,
     // exact)
     float vfac = 1.0f, vfac_inv = 1.0f;
+    // INT8 key cache, FP16 tiles: the key scales enter the staged K likewise
+    // (kfac), and the scores are multiplied back by kfac_inv (exact)
+    float kfac = 1.0f, kfac_inv = 1.0f;
 
     // ---- tile loader ------------------------------------------------------------
     // Register path (gload / lstore; the direct loads are `dma` below).
@@ -310,6 +313,7 @@ void attn_fwd_kernel(FwdArgs a) {
         u32x4 vreg[VB][4];
         u32x2 v8reg[VB][4];     // INT8 V cache: 8 codes of each of 4 keys
         u32x4 svk[VB];          // ... and the scales of those 4 keys
+        float skrow[K8CH];      // INT8 K cache, FP16 tiles: the scale of each chunk's key
         u32x4 skreg;
     };
     // The two-set pipeline waits for the older set with a load count, so every
@@ -378,8 +382,18 @@ void attn_fwd_kernel(FwdArgs a) {
                 if (K8TOT % NT == 0 || c < K8TOT)
                     kreg[n] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(k8rs, c * 16, 0, 0));
             }
-            if (tid < BN / 4) {
-                const __amdgpu_buffer_rsrc_t skrs = tile_rsrc(skb, Lk * 4, TBS, kt);
+            const __amdgpu_buffer_rsrc_t skrs = tile_rsrc(skb, Lk * 4, TBS, kt);
+            if (KV8 && !i8) {
+                // FP16 tiles of a key cache: the scale of each chunk's key (the
+                // staged tile holds code * s_k * kfac)
+#pragma unroll
+                for (int n = 0; n < K8CH; ++n) {
+                    const int c = tid + n * NT;
+                    if (K8TOT % NT == 0 || c < K8TOT)
+                        sg.skrow[n] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                            skrs, (c / (HD / 16)) * 4, 0, 0));
+                }
+            } else if (tid < BN / 4) {
                 skreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(skrs, tid * 16, 0, 0));
             }
         } else {
@@ -431,7 +445,7 @@ void attn_fwd_kernel(FwdArgs a) {
         char* kbuf = smem + (stage * KS + kgp) * STG;
         _Float16* vt = (_Float16*)(kbuf + L::KREG);
         float* scl = (float*)(kbuf + L::KREG + L::VBYTES);
-        if ((KV8 || (ROUTED && i8 && !ATTN_FUSED_KQUANT)) && tid < BN / 4)
+        if (((KV8 && i8) || (ROUTED && i8 && !ATTN_FUSED_KQUANT)) && tid < BN / 4)
             *(f32x4*)(scl + 4 * tid) = __builtin_bit_cast(f32x4, skreg) * a.c;
         if (ROUTED && i8 && !KV8 && ATTN_FUSED_KQUANT) {
             // the fp16 K tile quantised here: the HD/8 consecutive lanes that
@@ -479,6 +493,7 @@ void attn_fwd_kernel(FwdArgs a) {
             }
         } else if (KV8) {
             // FP16 route on an INT8 key cache: the codes widened to fp16 (exact)
+            // and scaled per key (below)
             _Float16* k16 = (_Float16*)kbuf;
 #pragma unroll
             for (int n = 0; n < K8CH; ++n) {
@@ -486,8 +501,19 @@ void attn_fwd_kernel(FwdArgs a) {
                 const int row = c / (HD / 16);
                 const int col = (c % (HD / 16)) * 16;
                 if (K8TOT % NT == 0 || c < K8TOT) {
-                    const u32x2 w0 = widen_i8x4(kreg[n][0]), w1 = widen_i8x4(kreg[n][1]);
-                    const u32x2 w2 = widen_i8x4(kreg[n][2]), w3 = widen_i8x4(kreg[n][3]);
+                    // widened codes times the key's scale times kfac, in fp16
+                    // (the products stay below 2^8)
+                    const float ks = sg.skrow[n] * kfac;
+                    const f16x2 h = {(_Float16)ks, (_Float16)ks};
+                    // (one product per widened word: a u32x2 built from two f16x2
+                    // products in one expression came out as the first product twice)
+                    auto mul = [&](unsigned w) { return __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, w) * h); };
+                    auto wide = [&](unsigned w) __attribute__((always_inline)) {
+                        const u32x2 p2 = widen_i8x4(w);
+                        return u32x2{mul(p2[0]), mul(p2[1])};
+                    };
+                    const u32x2 w0 = wide(kreg[n][0]), w1 = wide(kreg[n][1]);
+                    const u32x2 w2 = wide(kreg[n][2]), w3 = wide(kreg[n][3]);
                     *(u32x4*)(k16 + row * L::KP + col) = u32x4{w0[0], w0[1], w1[0], w1[1]};
                     *(u32x4*)(k16 + row * L::KP + col + 8) = u32x4{w2[0], w2[1], w3[0], w3[1]};
                 }
@@ -758,13 +784,9 @@ void attn_fwd_kernel(FwdArgs a) {
                     for (int i = 0; i < 16; ++i) x[kb32][i] = acc[i];
                 }
             }
-            amul = a.c;
-            if constexpr (KV8) {
-                // scores against the widened codes, times s_k * |scale| * log2(e)
-#pragma unroll
-                for (int kb32 = 0; kb32 < NKB; ++kb32) key_scale(kb32);
-                amul = 1.0f;
-            }
+            // on a key cache the staged keys are code * s_k * kfac (kfac a power of two)
+            amul = KV8 ? a.c * kfac_inv : a.c;
+
         }
 
         if constexpr (MASK) {
@@ -887,25 +909,46 @@ void attn_fwd_kernel(FwdArgs a) {
         // brought to [1, 2) at their largest by an exact power of two:
         // code * s_v * vfac stays below 2^8 (no overflow for any scale), and
         // keys whose scale is near the largest keep full fp16 precision
-        // whatever the value magnitude (no subnormal values).
-        float mx = 0.0f;
+        // whatever the value magnitude (no subnormal values).  The key-cache
+        // scales of FP16 tiles are normalised the same way.
+        float mx = 0.0f, mk = 0.0f;
         const int j1 = min(kt1 * BN, Lk);
-        for (int j = kt0 * BN + (int)threadIdx.x; j < j1; j += NW * KS * 64) mx = fmaxf(mx, fabsf(svb[j]));
+        for (int j = kt0 * BN + (int)threadIdx.x; j < j1; j += NW * KS * 64) {
+            mx = fmaxf(mx, fabsf(svb[j]));
+            mk = fmaxf(mk, fabsf(skb[j]));
+        }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        for (int o = 32; o > 0; o >>= 1) {
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+            mk = fmaxf(mk, __shfl_xor(mk, o));
+        }
         float* red = (float*)smem;
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+        if ((threadIdx.x & 63) == 0) {
+            red[2 * (threadIdx.x >> 6)] = mx;
+            red[2 * (threadIdx.x >> 6) + 1] = mk;
+        }
         __syncthreads();
         mx = 0.0f;
+        mk = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NW * KS; ++i) mx = fmaxf(mx, red[i]);
-        __syncthreads();
-        const int e = (int)((u_from_f(mx) >> 23) & 0xffu);    // biased exponent
-        if (e != 0 && e != 255) {
-            const int sh = max(-126, min(126, 127 - e));       // mx * 2^sh in [1, 2)
-            vfac = f_from_u((unsigned)(127 + sh) << 23);
-            vfac_inv = f_from_u((unsigned)(127 - sh) << 23);
+        for (int i = 0; i < NW * KS; ++i) {
+            mx = fmaxf(mx, red[2 * i]);
+            mk = fmaxf(mk, red[2 * i + 1]);
         }
+        __syncthreads();
+        // a power of two f and its inverse with m * f in [1, 2) (1 and 1 for
+        // a zero or non-finite m)
+        auto pow2_norm = [](float m, float& f, float& f_inv) __attribute__((always_inline)) {
+            const int e = (int)((u_from_f(m) >> 23) & 0xffu);    // biased exponent
+            if (e != 0 && e != 255) {
+                const int sh = max(-126, min(126, 127 - e));       // m * 2^sh in [1, 2)
+                f = f_from_u((unsigned)(127 + sh) << 23);
+                f_inv = f_from_u((unsigned)(127 - sh) << 23);
+            }
+        };
+        pow2_norm(mx, vfac, vfac_inv);
+        pow2_norm(mk, kfac, kfac_inv);
+
     }
     auto query_prologue = [&]() __attribute__((always_inline)) {
         if (a.neg) {
