@@ -119,14 +119,15 @@ attn_status attn_fwd_stream(const void* q, const void* k, const void* v, void* o
  *   k8, v8: device int8 in the layout of k and v; 16-byte aligned.
  *   k_scale, v_scale: device fp32, one per K / V row ([B, n_kvh, ksl] dense,
  *   [n_kvh, T] packed); 4-byte aligned.
- * attn_quantize_rows builds such a cache from fp16 rows.  The value scales
- * are applied to the fp16 probabilities that multiply the codes, after
- * division by a power of two near the largest |v_scale| of the keys a
- * workgroup visits (multiplied back, exactly, at the end), so any finite
- * v_scale works without overflow, and the precision of p * v_scale in fp16
- * depends only on the ratio of v_scale to that largest scale, not on the
- * values' magnitude.  Errors as attn_fwd (ATTN_ERR_NULL names the cache
- * pointers). */
+ * attn_quantize_rows builds such a cache from fp16 rows.  The value codes
+ * (and, for FP16 cells, the key codes) are multiplied by their row's scale
+ * in fp16 as the kernel stages them, after division of the scales by a
+ * power of two near the largest |v_scale| (|k_scale|) of the keys a
+ * workgroup visits (multiplied back, exactly, in fp32), so any finite scale
+ * works without overflow, and the precision of the staged values depends
+ * only on the ratio of a row's scale to that largest scale, not on the
+ * values' magnitude.  INT8 cells use the codes and k_scale as they are.
+ * Errors as attn_fwd (ATTN_ERR_NULL names the cache pointers). */
 attn_status attn_fwd_kv8(const void* q, const int8_t* k8, const float* k_scale,
                          const int8_t* v8, const float* v_scale, void* out,
                          int32_t B, int32_t qsl, int32_t ksl, int32_t hdim,
